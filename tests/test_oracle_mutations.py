@@ -1,0 +1,65 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (on the CPU only),
+compiles the mutant, swaps it in for the real library and reruns a set of the
+pins from test_oracle_pins.  Every mutant must fail at least one of them.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "nbw_oracle.c")
+
+MUTANTS = {
+    "lsb_first_planes": ("(codes[i * k + j] >> (7 - p)) & 1", "(codes[i * k + j] >> p) & 1"),
+    "natural_bit_order": ("(int)(e / 2 + 16 * (e % 2))", "(int)e"),
+    "group_major_tiles": ("((i / 16) * groups + g) * 256",
+                          "(g * (padded_rows(n) / 16) + i / 16) * 256"),
+    "dropped_half": ("((double)q + 0.5 - ldexp(1.0, r - 1))", "((double)q - ldexp(1.0, r - 1))"),
+    "wrong_exponent": ("s * ldexp(1.0, 8 - r)", "s * ldexp(1.0, 7 - r)"),
+    "shifted_scale_group": ("double s = nbwo_bf16_to_double(scales[i * groups + j / 128]);\n        wrow",
+                            "double s = nbwo_bf16_to_double(scales[i * groups + (j / 128 + 1) % groups]);\n        wrow"),
+    "transposed_x": ("nbwo_bf16_to_double(x[b * k + j])", "nbwo_bf16_to_double(x[j * batch + b])"),
+    "wrong_sign": ("acc += nbwo_bf16_to_double", "acc -= nbwo_bf16_to_double"),
+    "lsb_first_unpack": ("v = 2 * v + read_bit(planes, n, k, p, i, j);",
+                         "v = v + (read_bit(planes, n, k, p, i, j) << p);"),
+}
+
+
+def _pin_calls():
+    calls = [pins.test_pack_roundtrip_r8_reconstructs_parent,
+             lambda: pins.test_child_codes_are_msb_slices(3),
+             lambda: pins.test_child_value_is_mean_of_parent_bucket(2),
+             pins.test_dequant_r8_is_parent_grid,
+             lambda: pins.test_qgemm_exact_rational_bruteforce(3),
+             lambda: pins.test_qgemm_second_route_without_planes(4),
+             lambda: pins.test_qgemm_identity_activations_give_weights(4)]
+    for row in pins._golden_layout():
+        calls.append(lambda row=row: pins.test_layout_worked_examples(*row))
+    return calls
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-shared", "-fPIC", str(mutant_c), "-o",
+                    str(so), "-lm"], check=True)
+    monkeypatch.setattr(oracle, "_lib", oracle._configure(ctypes.CDLL(str(so))))
+    failures = 0
+    for call in _pin_calls():
+        try:
+            call()
+        except (AssertionError, ValueError):
+            failures += 1
+    assert failures > 0, f"mutant {name} passed every pin"
