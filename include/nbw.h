@@ -1,0 +1,159 @@
+/*
+ * nbw.h -- C ABI of libnbw: sliced r-bit qgemm over nested bit-plane weights
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (MatGPTQ: Efficient and Accurate Inference over Nested Quantized
+ * Models; MatGPTQ: Accurate and Efficient Post-Training Matryoshka
+ * Quantization) serves one 8-bit "sliceable" parent checkpoint at several
+ * precisions: the r-bit child keeps the most significant bits of every parent
+ * code (v1 abstract; v2 Abstract), reads exactly r bits of weight data (v2
+ * Abstract; Table 1, row "Exact r-bit loading"), and is executed by kernels
+ * that support batch sizes beyond one (v2 Abstract; Figure 1, kernel speed-up
+ * over a dense matmul across bit-widths, shapes and batch sizes).
+ *
+ * Conventions for every entry point
+ *  - Every pointer argument that names tensor data is a DEVICE pointer,
+ *    allocated and owned by the caller, who keeps it alive until the work
+ *    queued on `stream` has completed.  The library keeps no pointer beyond
+ *    the call.  `stream` is a hipStream_t passed as void* (NULL = default
+ *    stream); work is queued asynchronously on it.
+ *  - Errors are returned as nbw_status.  All argument checks run on the host
+ *    before any device work is queued; on error nothing is queued.  NBW_EHIP
+ *    means a HIP runtime call failed: nbw_last_hip_error() returns its
+ *    hipError_t for the calling thread.  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as with any HIP launch.
+ *  - Calls are thread-safe.  Calls queued on different streams may overlap;
+ *    they share no library state apart from one device-property cache.
+ *
+ * Data formats
+ *  - Parent codes: uint8 [n][k] row-major, c in [0, 255].
+ *  - Child codes: q_r = c >> (8 - r), r in 1..8 (the MatGPTQ pages run 2..8).
+ *  - Bit-planes (layout NBW_LAYOUT_T16): eight planes, plane p holding bit
+ *    (7 - p) of every code, so plane 0 is the MSB and the r-bit child is the
+ *    byte prefix of r planes.  Rows are padded to a multiple of 16 (padding
+ *    bits 0); plane_bytes = ceil(n/16)*16 * k/8.  The 16-byte chunk of
+ *    (plane p, row i, group g = j/128) starts at
+ *        p*plane_bytes + ((i/16)*(k/128) + g)*256 + (i%16)*16,
+ *    and column c = j%128 of that chunk sits in little-endian 32-bit word c/32
+ *    at bit (c%32)/2 + 16*(c%2): even columns in bits 0..15, odd columns in
+ *    bits 16..31 of each word.  So one 16-row tile of one group is 256
+ *    contiguous bytes per plane, and the two columns of a bf16 pair sit at
+ *    the same bit of the two 16-bit halves of a word.
+ *  - Scales: bf16 [n][k/128] row-major, one per row and 128-wide group of k.
+ *  - Dequantisation of a child code (the pages state no formula; this library
+ *    uses the symmetric mid-point grid, which puts the child value at the
+ *    mean of its parent bucket):
+ *        w = s * 2^(8-r) * (q_r + 1/2 - 2^(r-1)).
+ *  - X: bf16 [batch][k] row-major.  Y: fp32 [batch][n] row-major,
+ *        Y[b][i] = sum_j X[b][j] * w[i][j]   (fp32 accumulation).
+ *  - k must be a positive multiple of 128; n >= 1; batch >= 0.
+ *
+ * Alignment: planes, X and Y 16 bytes; scales 2 bytes; codes 16 bytes.
+ */
+#ifndef NBW_H
+#define NBW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nbw_status {
+    NBW_OK = 0,
+    NBW_EINVAL = 1,       /* null pointer, bad size, k not a multiple of 128, batch < 1 */
+    NBW_EALIGN = 2,       /* a pointer misses its required alignment */
+    NBW_ERANGE = 3,       /* r outside 1..8, or r larger than the planes present */
+    NBW_EUNSUPPORTED = 4, /* unknown layout or kernel selector */
+    NBW_EHIP = 5          /* a HIP runtime call failed (see nbw_last_hip_error) */
+} nbw_status;
+
+#define NBW_LAYOUT_T16 1
+
+/* A view of packed weights: `nplanes` consecutive planes of `plane_bytes`
+ * each, starting at device pointer `planes` (plane 0 = MSB).  A parent view
+ * has nplanes = 8; an r-bit child view has nplanes = r and the same base. */
+typedef struct nbw_wview {
+    const void *planes;
+    int64_t n;           /* rows (output features) */
+    int64_t k;           /* columns (input features), multiple of 128 */
+    int32_t nplanes;     /* planes present at `planes` */
+    int32_t layout;      /* NBW_LAYOUT_T16 */
+    int64_t plane_bytes; /* ceil(n/16)*16*k/8 */
+} nbw_wview;
+
+/* Kernel selectors for nbw_qgemm_kernel (NBW_KERNEL_AUTO picks by batch). */
+typedef enum nbw_kernel {
+    NBW_KERNEL_AUTO = 0,
+    NBW_KERNEL_GEMV = 1,   /* VALU dequant + bf16 dot2, batch 1..2 per launch slice */
+    NBW_KERNEL_SMALLB = 2, /* in-register dequant feeding MFMA, 16 batch rows per slice */
+    NBW_KERNEL_GEMM = 3    /* large-batch MFMA kernel */
+} nbw_kernel;
+
+/* Bytes of one plane for an n x k matrix, or -1 if n < 1 or k is not a
+ * positive multiple of 128. */
+int64_t nbw_plane_bytes(int64_t n, int64_t k);
+
+/* Bytes read by an r-bit child: r * nbw_plane_bytes(n, k) (-1 on bad input). */
+int64_t nbw_packed_bytes(int64_t n, int64_t k, int32_t r);
+
+/* Pack parent codes into the 8 MSB-first bit-planes of layout NBW_LAYOUT_T16
+ * (MatGPTQ v2, Abstract and Table 1: one checkpoint whose r-bit child reads
+ * exactly r bits).  codes: device uint8 [n][k]; planes_out: device buffer of
+ * planes_out_bytes >= 8*nbw_plane_bytes(n, k), fully written (padding rows
+ * included).  Bit-exact; runs on `stream`. */
+nbw_status nbw_pack_bitplanes(const uint8_t *codes, int64_t n, int64_t k, void *planes_out,
+                              int64_t planes_out_bytes, void *stream);
+
+/* Describe `nplanes` planes (1..8) of an n x k matrix at device pointer
+ * `planes`.  Host only; no device work. */
+nbw_status nbw_make_view(const void *planes, int64_t n, int64_t k, int32_t nplanes,
+                         nbw_wview *out);
+
+/* The r-bit child of a view: same base pointer, nplanes = r (MatGPTQ v1
+ * abstract: lower precisions by slicing the most significant bits).  Host
+ * only; no device work, no data read.  NBW_ERANGE if r < 1 or
+ * r > parent->nplanes. */
+nbw_status nbw_slice_view(const nbw_wview *parent, int32_t r, nbw_wview *child);
+
+/* Y = X . dequant_r(W)^T for the r-bit child of `w` (reads planes 0..r-1
+ * only, plus the scales and X).  x_bf16: [batch][k]; scales_bf16:
+ * [n][k/128]; y: fp32 [batch][n], fully written.  batch == 0 is an empty
+ * product: NBW_OK, nothing queued, x/scales/y unused.  The kernel is chosen
+ * by batch size.  Runs on `stream`. */
+nbw_status nbw_qgemm(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                     const void *scales_bf16, int32_t r, float *y, void *stream);
+
+/* nbw_qgemm with an explicit kernel choice (every kernel accepts every batch
+ * size; used to test and time each kernel on its own). */
+nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                            const void *scales_bf16, int32_t r, float *y, nbw_kernel kernel,
+                            void *stream);
+
+/* Child codes q_r = c >> (8 - r) read back from planes 0..r-1 of `w`, through
+ * the same in-register plane decode the qgemm kernels use.  codes_out: device
+ * uint8 [n][k].  A test hook for the bit-exact slicing check. */
+nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, void *stream);
+
+/* Name of the kernel template instance nbw_qgemm_kernel would launch for
+ * this problem on the current device (for example "nbw::gemv_kernel<4, 1, 2>",
+ * as profilers print it without the parameter list), or "" on bad input.  The
+ * string lives until the calling thread's next call.  Host only; queries the
+ * device's compute-unit count once. */
+const char *nbw_kernel_name(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_kernel kernel);
+
+/* Static text for a status code. */
+const char *nbw_status_str(nbw_status s);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int32_t nbw_last_hip_error(void);
+
+/* Library version string. */
+const char *nbw_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NBW_H */

@@ -1,0 +1,228 @@
+"""nested_bit_weight_amd -- sliced r-bit qgemm over nested bit-plane weights, MI355X.
+
+A thin ctypes binding over ``libnbw.so`` (C ABI in ``include/nbw.h``).  It only
+marshals arguments: PyTorch provides device memory and the current stream; every
+step of the computation runs in the library's HIP kernels.  If the library is not
+built, every call raises -- there is no fallback path.
+
+    planes = pack_bitplanes(codes)            # uint8 [n][k] on the GPU -> PackedWeight
+    child = slice_view(planes, r)             # the r-bit child: same storage, r planes
+    y = qgemm(x, child, scales, r)            # x bf16 [B][k], scales bf16 [n][k/128] -> fp32 [B][n]
+
+(MatGPTQ: Efficient and Accurate Inference over Nested Quantized Models, Abstract:
+one sliceable parent; an r-bit model reads exactly r bits; kernels for batch sizes
+beyond one.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnbw.so")
+
+NBW_LAYOUT_T16 = 1
+KERNELS = {"auto": 0, "gemv": 1, "smallb": 2, "gemm": 3}
+_STATUS = {0: "NBW_OK", 1: "NBW_EINVAL", 2: "NBW_EALIGN", 3: "NBW_ERANGE",
+           4: "NBW_EUNSUPPORTED", 5: "NBW_EHIP"}
+
+
+class NBWError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        lib = _lib()
+        text = lib.nbw_status_str(status).decode()
+        extra = f" (hipError {lib.nbw_last_hip_error()})" if status == 5 else ""
+        super().__init__(f"{what}: {_STATUS.get(status, status)} {text}{extra}")
+
+
+class WView(ctypes.Structure):
+    _fields_ = [("planes", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("nplanes", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("plane_bytes", ctypes.c_int64)]
+
+
+_LIB = None
+
+EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
+           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_unpack_codes",
+           "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        pv = ctypes.POINTER(WView)
+        lib.nbw_plane_bytes.argtypes = [i64, i64]
+        lib.nbw_plane_bytes.restype = i64
+        lib.nbw_packed_bytes.argtypes = [i64, i64, i32]
+        lib.nbw_packed_bytes.restype = i64
+        lib.nbw_pack_bitplanes.argtypes = [vp, i64, i64, vp, i64, vp]
+        lib.nbw_pack_bitplanes.restype = ctypes.c_int
+        lib.nbw_make_view.argtypes = [vp, i64, i64, i32, pv]
+        lib.nbw_make_view.restype = ctypes.c_int
+        lib.nbw_slice_view.argtypes = [pv, i32, pv]
+        lib.nbw_slice_view.restype = ctypes.c_int
+        lib.nbw_qgemm.argtypes = [vp, i64, pv, vp, i32, vp, vp]
+        lib.nbw_qgemm.restype = ctypes.c_int
+        lib.nbw_qgemm_kernel.argtypes = [vp, i64, pv, vp, i32, vp, ctypes.c_int, vp]
+        lib.nbw_qgemm_kernel.restype = ctypes.c_int
+        lib.nbw_unpack_codes.argtypes = [pv, i32, vp, vp]
+        lib.nbw_unpack_codes.restype = ctypes.c_int
+        lib.nbw_status_str.argtypes = [ctypes.c_int]
+        lib.nbw_status_str.restype = ctypes.c_char_p
+        lib.nbw_last_hip_error.argtypes = []
+        lib.nbw_last_hip_error.restype = i32
+        lib.nbw_kernel_name.argtypes = [i64, i64, i64, i32, ctypes.c_int]
+        lib.nbw_kernel_name.restype = ctypes.c_char_p
+        lib.nbw_version.argtypes = []
+        lib.nbw_version.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes handle of libnbw.so (raises if it is not built)."""
+    return _lib()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise NBWError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def plane_bytes(n: int, k: int) -> int:
+    v = _lib().nbw_plane_bytes(n, k)
+    if v < 0:
+        raise ValueError(f"bad shape n={n}, k={k} (need n >= 1, k a positive multiple of 128)")
+    return int(v)
+
+
+def packed_bytes(n: int, k: int, r: int) -> int:
+    v = _lib().nbw_packed_bytes(n, k, r)
+    if v < 0:
+        raise ValueError(f"bad shape or bit-width n={n}, k={k}, r={r}")
+    return int(v)
+
+
+class PackedWeight:
+    """Bit-planes of an n x k weight: ``nplanes`` planes (8 = parent, r = child).
+
+    ``storage`` is the uint8 device tensor holding at least ``nplanes`` planes; a child
+    made by ``slice_view`` shares it."""
+
+    def __init__(self, storage: torch.Tensor, n: int, k: int, nplanes: int):
+        self.storage = storage
+        self.n, self.k, self.nplanes = n, k, nplanes
+        self.view = WView()
+        _check(_lib().nbw_make_view(ctypes.c_void_p(storage.data_ptr()), n, k, nplanes,
+                                    ctypes.byref(self.view)), "nbw_make_view")
+
+    @property
+    def plane_bytes(self) -> int:
+        return int(self.view.plane_bytes)
+
+    @property
+    def nbytes(self) -> int:
+        """Bytes of plane data this view reads (nplanes * plane_bytes)."""
+        return self.nplanes * self.plane_bytes
+
+    def slice_view(self, r: int) -> "PackedWeight":
+        return slice_view(self, r)
+
+    def __repr__(self):
+        return f"PackedWeight(n={self.n}, k={self.k}, nplanes={self.nplanes})"
+
+
+def pack_bitplanes(codes: torch.Tensor, out: torch.Tensor | None = None) -> PackedWeight:
+    """uint8 parent codes [n][k] (GPU) -> 8-plane PackedWeight."""
+    _need(codes, "codes", torch.uint8, 2)
+    n, k = codes.shape
+    need = 8 * plane_bytes(n, k)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=codes.device)
+    else:
+        _need(out, "out", torch.uint8, 1)
+        if out.numel() < need or out.device != codes.device:
+            raise ValueError("out is too small or on another device")
+    _check(_lib().nbw_pack_bitplanes(ctypes.c_void_p(codes.data_ptr()), n, k,
+                                     ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                     _stream(codes)), "nbw_pack_bitplanes")
+    return PackedWeight(out, n, k, 8)
+
+
+def slice_view(w: PackedWeight, r: int) -> PackedWeight:
+    """The r-bit child of ``w``: the first r planes of the same storage (host only)."""
+    child = WView()
+    _check(_lib().nbw_slice_view(ctypes.byref(w.view), r, ctypes.byref(child)), "nbw_slice_view")
+    out = PackedWeight.__new__(PackedWeight)
+    out.storage, out.n, out.k, out.nplanes, out.view = w.storage, w.n, w.k, r, child
+    return out
+
+
+def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
+          out: torch.Tensor | None = None, kernel: str = "auto") -> torch.Tensor:
+    """fp32 Y [B][n] = X . dequant_r(W)^T for the r-bit child of ``w``."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(scales, "scales", torch.bfloat16, 2)
+    b, k = x.shape
+    if k != w.k:
+        raise ValueError(f"x has k={k}, weights have k={w.k}")
+    if tuple(scales.shape) != (w.n, w.k // 128):
+        raise ValueError(f"scales must be [{w.n}][{w.k // 128}], got {tuple(scales.shape)}")
+    if scales.device != x.device or w.storage.device != x.device:
+        raise ValueError("x, scales and weights must be on the same GPU")
+    if out is None:
+        out = torch.empty((b, w.n), dtype=torch.float32, device=x.device)
+    else:
+        _need(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (b, w.n) or out.device != x.device:
+            raise ValueError(f"out must be [{b}][{w.n}] on the same GPU")
+    _check(_lib().nbw_qgemm_kernel(ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(w.view),
+                                   ctypes.c_void_p(scales.data_ptr()), r,
+                                   ctypes.c_void_p(out.data_ptr()), KERNELS[kernel], _stream(x)),
+           "nbw_qgemm")
+    return out
+
+
+def unpack_codes(w: PackedWeight, r: int) -> torch.Tensor:
+    """Child codes q_r [n][k] (uint8) decoded on the GPU from planes 0..r-1 (test hook)."""
+    out = torch.empty((w.n, w.k), dtype=torch.uint8, device=w.storage.device)
+    _check(_lib().nbw_unpack_codes(ctypes.byref(w.view), r, ctypes.c_void_p(out.data_ptr()),
+                                   _stream(out)), "nbw_unpack_codes")
+    return out
+
+
+def kernel_name(batch: int, n: int, k: int, r: int, kernel: str = "auto") -> str:
+    """Name of the kernel instance nbw_qgemm would launch (as profilers print it)."""
+    return _lib().nbw_kernel_name(batch, n, k, r, KERNELS[kernel]).decode()
+
+
+def version() -> str:
+    return _lib().nbw_version().decode()
+
+
+__all__ = ["pack_bitplanes", "slice_view", "qgemm", "unpack_codes", "plane_bytes",
+           "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
+           "version"]

@@ -1,0 +1,196 @@
+// abi.hip -- the extern "C" entry points of libnbw (see include/nbw.h).
+//
+// Host code only: argument validation, weight views, kernel choice by batch
+// size, and launches on the caller's stream.  Every check runs before any
+// HIP call, so a rejected call queues nothing.
+#include <climits>
+#include <mutex>
+#include <vector>
+
+#include "launch.h"
+#include "nbw.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+nbw_status hip_failed(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return NBW_EHIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool shape_ok(int64_t n, int64_t k) {
+    return n >= 1 && n <= INT_MAX - 16 && k >= 128 && k % 128 == 0 && k <= INT_MAX;
+}
+
+// Compute-unit count of the current device, cached per device.
+nbw_status cu_count(int *out) {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_failed(e);
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int v = 0;
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_failed(e);
+        cache[dev] = v > 0 ? v : 1;
+    }
+    *out = cache[dev];
+    return NBW_OK;
+}
+
+nbw_status check_view(const nbw_wview *w) {
+    if (!w || !w->planes) return NBW_EINVAL;
+    if (!shape_ok(w->n, w->k)) return NBW_EINVAL;
+    if (w->layout != NBW_LAYOUT_T16) return NBW_EUNSUPPORTED;
+    if (w->nplanes < 1 || w->nplanes > 8) return NBW_ERANGE;
+    if (w->plane_bytes != nbw_plane_bytes(w->n, w->k)) return NBW_EINVAL;
+    if (!aligned(w->planes, 16)) return NBW_EALIGN;
+    return NBW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nbw_plane_bytes(int64_t n, int64_t k) {
+    if (!shape_ok(n, k)) return -1;
+    return (n + 15) / 16 * 16 * (k / 8);
+}
+
+int64_t nbw_packed_bytes(int64_t n, int64_t k, int32_t r) {
+    const int64_t pb = nbw_plane_bytes(n, k);
+    if (pb < 0 || r < 1 || r > 8) return -1;
+    return r * pb;
+}
+
+nbw_status nbw_pack_bitplanes(const uint8_t *codes, int64_t n, int64_t k, void *planes_out,
+                              int64_t planes_out_bytes, void *stream) {
+    if (!codes || !planes_out) return NBW_EINVAL;
+    if (!shape_ok(n, k)) return NBW_EINVAL;
+    const int64_t pb = nbw_plane_bytes(n, k);
+    if (planes_out_bytes < 8 * pb) return NBW_EINVAL;
+    if (!aligned(codes, 16) || !aligned(planes_out, 16)) return NBW_EALIGN;
+    hipError_t e = nbw::launch_pack(codes, (int)n, (int)k, (uint8_t *)planes_out, pb,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+nbw_status nbw_make_view(const void *planes, int64_t n, int64_t k, int32_t nplanes,
+                         nbw_wview *out) {
+    if (!out || !planes) return NBW_EINVAL;
+    if (!shape_ok(n, k)) return NBW_EINVAL;
+    if (nplanes < 1 || nplanes > 8) return NBW_ERANGE;
+    if (!aligned(planes, 16)) return NBW_EALIGN;
+    out->planes = planes;
+    out->n = n;
+    out->k = k;
+    out->nplanes = nplanes;
+    out->layout = NBW_LAYOUT_T16;
+    out->plane_bytes = nbw_plane_bytes(n, k);
+    return NBW_OK;
+}
+
+nbw_status nbw_slice_view(const nbw_wview *parent, int32_t r, nbw_wview *child) {
+    if (!child) return NBW_EINVAL;
+    nbw_status st = check_view(parent);
+    if (st != NBW_OK) return st;
+    if (r < 1 || r > parent->nplanes) return NBW_ERANGE;
+    *child = *parent;
+    child->nplanes = r;
+    return NBW_OK;
+}
+
+nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                            const void *scales_bf16, int32_t r, float *y, nbw_kernel kernel,
+                            void *stream) {
+    nbw_status st = check_view(w);
+    if (st != NBW_OK) return st;
+    if (batch < 0) return NBW_EINVAL;
+    if (r < 1 || r > 8 || r > w->nplanes) return NBW_ERANGE;
+    if (kernel < NBW_KERNEL_AUTO || kernel > NBW_KERNEL_GEMM) return NBW_EUNSUPPORTED;
+    if (batch == 0) return NBW_OK;  // empty product: nothing to read or write
+    if (!x_bf16 || !scales_bf16 || !y) return NBW_EINVAL;
+    if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scales_bf16, 2)) return NBW_EALIGN;
+    int cus = 0;
+    st = cu_count(&cus);
+    if (st != NBW_OK) return st;
+    if (kernel == NBW_KERNEL_AUTO)
+        kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
+    nbw::QgemmArgs a;
+    a.x = (const uint16_t *)x_bf16;
+    a.batch = batch;
+    a.planes = (const uint8_t *)w->planes;
+    a.plane_bytes = w->plane_bytes;
+    a.scales = (const uint16_t *)scales_bf16;
+    a.n = (int)w->n;
+    a.k = (int)w->k;
+    a.y = y;
+    hipError_t e;
+    switch (kernel) {
+    case NBW_KERNEL_GEMV: e = nbw::launch_gemv(r, a, cus, (hipStream_t)stream); break;
+    case NBW_KERNEL_SMALLB: e = nbw::launch_smallb(r, a, cus, (hipStream_t)stream); break;
+    default: e = nbw::launch_gemm(r, a, cus, (hipStream_t)stream); break;
+    }
+    return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+nbw_status nbw_qgemm(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                     const void *scales_bf16, int32_t r, float *y, void *stream) {
+    return nbw_qgemm_kernel(x_bf16, batch, w, scales_bf16, r, y, NBW_KERNEL_AUTO, stream);
+}
+
+nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, void *stream) {
+    if (!codes_out) return NBW_EINVAL;
+    nbw_status st = check_view(w);
+    if (st != NBW_OK) return st;
+    if (r < 1 || r > 8 || r > w->nplanes) return NBW_ERANGE;
+    if (!aligned(codes_out, 16)) return NBW_EALIGN;
+    hipError_t e = nbw::launch_unpack(r, (const uint8_t *)w->planes, w->plane_bytes, (int)w->n,
+                                      (int)w->k, codes_out, (hipStream_t)stream);
+    return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+const char *nbw_kernel_name(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_kernel kernel) {
+    thread_local char buf[96];
+    if (!shape_ok(n, k) || batch < 1 || r < 1 || r > 8 || kernel < NBW_KERNEL_AUTO ||
+        kernel > NBW_KERNEL_GEMM)
+        return "";
+    int cus = 0;
+    if (cu_count(&cus) != NBW_OK) return "";
+    if (kernel == NBW_KERNEL_AUTO)
+        kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
+    nbw::QgemmArgs a = {};
+    a.batch = batch;
+    a.n = (int)n;
+    a.k = (int)k;
+    switch (kernel) {
+    case NBW_KERNEL_GEMV: nbw::gemv_name(r, a, cus, buf, sizeof buf); break;
+    case NBW_KERNEL_SMALLB: nbw::smallb_name(r, a, cus, buf, sizeof buf); break;
+    default: nbw::gemm_name(r, a, cus, buf, sizeof buf); break;
+    }
+    return buf;
+}
+
+const char *nbw_status_str(nbw_status s) {
+    switch (s) {
+    case NBW_OK: return "ok";
+    case NBW_EINVAL: return "invalid argument";
+    case NBW_EALIGN: return "misaligned pointer";
+    case NBW_ERANGE: return "bit-width out of range";
+    case NBW_EUNSUPPORTED: return "unsupported layout or kernel";
+    case NBW_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t nbw_last_hip_error(void) { return g_last_hip_error; }
+
+const char *nbw_version(void) { return "nbw 0.1.0 gfx950"; }
+
+}  // extern "C"

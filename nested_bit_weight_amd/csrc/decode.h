@@ -1,0 +1,244 @@
+// decode.h -- in-register decode of MSB-first bit-planes into bf16 MFMA/dot2
+// operands, for gfx950.
+//
+// The r-bit child of a parent code keeps its top r bits (MatGPTQ: Accurate and
+// Efficient Post-Training Matryoshka Quantization, abstract: slicing the most
+// significant bits), and reads exactly r planes (MatGPTQ: Efficient and
+// Accurate Inference over Nested Quantized Models, Abstract; Table 1, "Exact
+// r-bit loading").  The kernels therefore receive, per 32 columns of one row,
+// r 32-bit words P_0..P_{r-1} (P_0 = MSB plane) in the library layout: column
+// e of the 32 sits at bit e/2 + 16*(e%2), so the column pair (2m, 2m+1) sits at
+// bits (m, m+16) -- the two 16-bit halves of a bf16 pair.
+//
+// Decoding runs in two phases, both plain 32-bit VALU work:
+//
+//  1. A bit-matrix transpose network of delta swaps ("merge", below) turns up
+//     to four plane words into words whose 1-, 2- or 4-bit fields each hold
+//     one column's code, MSB first.  A merge of words a, b at distance d with
+//     mask m is its own inverse, so the packer runs the same network backwards.
+//
+//  2. Each output word D_m (the bf16 pair of columns 2m, 2m+1) is cut out of a
+//     network word with one shift and one and-or:
+//         D_m = ((Z >> shift) & mask) | MAGIC
+//     where MAGIC holds the bf16 exponent 2^E in both halves and the code lands
+//     in the mantissa.  With the code's least significant bit at mantissa bit
+//     `lsb`, the bf16 value is exactly 2^E + q * 2^(E - 7 + lsb).  E is chosen
+//     per pair so that the coefficient of q is the same power of two for every
+//     column; the per-column constant 2^E ("offset") is removed afterwards by
+//     a correction that depends only on X (sum_k x_k * offset_k), computed
+//     once per group and batch row and shared by every weight row.  All
+//     operands are exact: q has at most 4 bits per phase, well inside bf16's
+//     8-bit significand.
+//
+// Codes wider than 4 bits (r = 5..8) are decoded as two phases of at most 4
+// planes: planes 0..3 (coefficient 2^(r-4)) and planes 4..r-1 (coefficient 1),
+// whose products sum to the full code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nbw {
+
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- network
+
+// Delta swap: hi takes a's bits under m and b's bits (shifted down by d) under
+// ~m; lo takes a's bits under ~m (shifted up by d) and b's bits under ~m.
+__host__ __device__ __forceinline__ void merge(uint32_t a, uint32_t b, int d, uint32_t m, uint32_t &hi,
+                                      uint32_t &lo) {
+    hi = (a & m) | ((b >> d) & ~m);
+    lo = ((a << d) & m) | (b & ~m);
+}
+
+constexpr uint32_t M1 = 0xAAAAAAAAu;
+constexpr uint32_t M2 = 0xCCCCCCCCu;
+constexpr uint32_t M4 = 0xF0F0F0F0u;
+
+// Number of network words produced for RP planes (1..4).
+template <int RP> struct NetWords { static constexpr int value = RP == 1 ? 1 : RP == 2 ? 2 : 4; };
+
+// Phase 1 for RP planes (1..4).  Output word index w and field layout:
+//  RP = 1: w0 = P0; bit b is column position b.
+//  RP = 2: w0 = even positions, w1 = odd positions; field j (bits 2j..2j+1)
+//          of w_t is the code of position 2j + t.
+//  RP = 3, 4: w_s (s = 0..3); nibble j (bits 4j..4j+3) of w_s is the code of
+//          position 4j + s (for RP = 3 the nibble is (code << 1)).
+template <int RP>
+__host__ __device__ __forceinline__ void network(const uint32_t *P, uint32_t *Z) {
+    if constexpr (RP == 1) {
+        Z[0] = P[0];
+    } else if constexpr (RP == 2) {
+        merge(P[0], P[1], 1, M1, Z[1], Z[0]);
+    } else {
+        uint32_t h01, l01, h23, l23;
+        merge(P[0], P[1], 1, M1, h01, l01);
+        if constexpr (RP == 4) {
+            merge(P[2], P[3], 1, M1, h23, l23);
+        } else {
+            h23 = P[2] & M1;
+            l23 = (P[2] << 1) & M1;
+        }
+        merge(h01, h23, 2, M2, Z[3], Z[1]);
+        merge(l01, l23, 2, M2, Z[2], Z[0]);
+    }
+}
+
+// ---------------------------------------------------------------- extraction plan
+
+// For pair m (0..15) of an RP-plane phase: which network word, the right
+// shift, and the bit of the code's LSB inside each 16-bit half after the shift.
+struct Pick {
+    int word, shift, lsb;
+};
+
+template <int RP> __host__ __device__ constexpr Pick pick(int m) {
+    if (RP == 1) {
+        int sh = m < 7 ? 0 : (m < 14 ? 7 : 14);
+        return Pick{0, sh, m - sh};
+    } else if (RP == 2) {
+        int t = m & 1, j = m >> 1;
+        int sh = j < 3 ? 0 : (j < 6 ? 6 : 12);
+        return Pick{t, sh, 2 * j - sh};
+    } else {
+        int s = m & 3, j = m >> 2;
+        int sh = j == 0 ? 0 : 4 * j - 3;
+        int nib = j == 0 ? 0 : 3;      // nibble's bit 0 after the shift
+        return Pick{s, sh, nib + (RP == 3 ? 1 : 0)};
+    }
+}
+
+template <int RP> __host__ __device__ constexpr uint32_t pick_mask(int m) {
+    uint32_t f = ((1u << RP) - 1u) << pick<RP>(m).lsb;
+    return f | (f << 16);
+}
+
+// bf16 exponent field value (biased) for pair m, code coefficient 2^C.
+template <int RP, int C> __host__ __device__ constexpr uint32_t pick_expo(int m) {
+    return (uint32_t)(127 + C + 7 - pick<RP>(m).lsb);
+}
+
+template <int RP, int C> __host__ __device__ constexpr uint32_t pick_magic(int m) {
+    uint32_t h = pick_expo<RP, C>(m) << 7;
+    return h | (h << 16);
+}
+
+// The constant part (offset) of pair m's bf16 values, as a bf16 pair bit
+// pattern (offset = 2^(C + 7 - lsb), the magic with an all-zero code).
+template <int RP, int C> __host__ __device__ constexpr uint32_t pick_offset_pair(int m) {
+    return pick_magic<RP, C>(m);
+}
+
+// Phase 2 for one pair.
+template <int RP, int C>
+__host__ __device__ __forceinline__ uint32_t extract(const uint32_t *Z, int m) {
+    const Pick p = pick<RP>(m);
+    uint32_t z = Z[p.word];
+    if (p.shift) z >>= p.shift;
+    return (z & pick_mask<RP>(m)) | pick_magic<RP, C>(m);
+}
+
+// Decode one 32-column word set of RP planes into 16 bf16 pairs (column pairs
+// 2m, 2m+1 for m = 0..15), code coefficient 2^C.
+template <int RP, int C>
+__host__ __device__ __forceinline__ void decode_phase(const uint32_t *P, uint32_t *D) {
+    uint32_t Z[NetWords<RP>::value];
+    network<RP>(P, Z);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) D[m] = extract<RP, C>(Z, m);
+}
+
+// Number of phases for an r-bit child and the planes in each.
+template <int R> struct Phases {
+    static constexpr int count = R <= 4 ? 1 : 2;
+    static constexpr int rp0 = R <= 4 ? R : 4;   // planes 0..rp0-1
+    static constexpr int rp1 = R <= 4 ? 0 : R - 4; // planes 4..R-1
+    static constexpr int c0 = R <= 4 ? 0 : R - 4; // coefficient exponent of phase 0
+};
+
+// Sum over the 16 pairs of one word set of offset_m * (x_lo + x_hi), for both
+// phases: the constant the decoded operands add to sum_k x_k * q_k.
+template <int R>
+__device__ __forceinline__ float offset_dot(const uint32_t *X2, float acc) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        uint32_t off = pick_offset_pair<Phases<R>::rp0, Phases<R>::c0>(m);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, off),
+                                              __builtin_bit_cast(bf16x2_t, X2[m]), acc, false);
+        if constexpr (Phases<R>::count == 2) {
+            uint32_t off1 = pick_offset_pair<Phases<R>::rp1, 0>(m);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, off1),
+                                                  __builtin_bit_cast(bf16x2_t, X2[m]), acc,
+                                                  false);
+        }
+    }
+    return acc;
+}
+
+// Sum of the 32 x values held as 16 bf16 pairs.
+__device__ __forceinline__ float pair_sum(const uint32_t *X2, float acc) {
+    const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
+                                              __builtin_bit_cast(bf16x2_t, X2[m]), acc, false);
+    return acc;
+}
+
+// Decode the r-bit codes of one word set into D0 (phase 0) and D1 (phase 1,
+// R > 4 only).  P: R plane words, P[p] = plane p.
+template <int R>
+__host__ __device__ __forceinline__ void decode_word(const uint32_t *P, uint32_t *D0, uint32_t *D1) {
+    decode_phase<Phases<R>::rp0, Phases<R>::c0>(P, D0);
+    if constexpr (Phases<R>::count == 2) decode_phase<Phases<R>::rp1, 0>(P + 4, D1);
+}
+
+// Raw codes (no bf16) of pair m for an RP-plane phase: low half and high half.
+template <int RP>
+__host__ __device__ __forceinline__ uint32_t extract_codes(const uint32_t *Z, int m) {
+    const Pick p = pick<RP>(m);
+    uint32_t z = Z[p.word];
+    if (p.shift) z >>= p.shift;
+    z = (z & pick_mask<RP>(m)) >> p.lsb;
+    return z;  // code(2m) in bits 0..RP-1, code(2m+1) in bits 16..16+RP-1
+}
+
+// ---------------------------------------------------------------- packing
+
+// Byte `b` (0..3) of w.
+__host__ __device__ __forceinline__ uint32_t byte_of(uint32_t w, int b) { return (w >> (8 * b)) & 0xFFu; }
+
+// 32 codes (8 words, word q = columns 4q..4q+3) -> 8 plane words.
+__host__ __device__ __forceinline__ void pack_word32(const uint32_t *W, uint32_t *P) {
+    // Y_t: byte j holds the code at plane-bit position 8j + t, i.e. columns
+    // 2t (j=0), 16+2t (j=1), 2t+1 (j=2), 17+2t (j=3).
+    uint32_t Y[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t a = W[t >> 1], c = W[4 + (t >> 1)];
+        const int b0 = 2 * (t & 1);
+        Y[t] = byte_of(a, b0) | (byte_of(c, b0) << 8) | (byte_of(a, b0 + 1) << 16) |
+               (byte_of(c, b0 + 1) << 24);
+    }
+    // Undo the byte-level merge: (B_hi = Y[4+s], B_lo = Y[s]) -> (Z_s, Z'_s).
+    uint32_t Z[4], Zp[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) merge(Y[4 + s], Y[s], 4, M4, Z[s], Zp[s]);
+    // Undo the nibble-level merges.
+    uint32_t h01, h23, l01, l23, h45, h67, l45, l67;
+    merge(Z[3], Z[1], 2, M2, h01, h23);
+    merge(Z[2], Z[0], 2, M2, l01, l23);
+    merge(Zp[3], Zp[1], 2, M2, h45, h67);
+    merge(Zp[2], Zp[0], 2, M2, l45, l67);
+    // Undo the pair-level merges.
+    merge(h01, l01, 1, M1, P[0], P[1]);
+    merge(h23, l23, 1, M1, P[2], P[3]);
+    merge(h45, l45, 1, M1, P[4], P[5]);
+    merge(h67, l67, 1, M1, P[6], P[7]);
+}
+
+}  // namespace nbw

@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI: no GPU needed, no device work queued.
+
+The library must load, export every entry point include/nbw.h declares, and
+reject bad arguments with the documented status codes before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nested_bit_weight_amd as nbw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nbw.h")
+
+OK, EINVAL, EALIGN, ERANGE, EUNSUPPORTED = 0, 1, 2, 3, 4
+FAKE = 0x7F0000001000  # a 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nbw.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^(\n]*?\b(nbw_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in nbw.h but not exported"
+    assert set(names) == set(nbw.EXPORTS)
+
+
+def test_plane_bytes(lib):
+    assert lib.nbw_plane_bytes(1, 128) == 16 * 16
+    assert lib.nbw_plane_bytes(16, 4096) == 16 * 512
+    assert lib.nbw_plane_bytes(17, 4096) == 32 * 512
+    assert lib.nbw_plane_bytes(0, 128) == -1
+    assert lib.nbw_plane_bytes(16, 100) == -1
+    assert lib.nbw_packed_bytes(6144, 4096, 3) == 3 * 6144 * 512
+    assert lib.nbw_packed_bytes(16, 128, 9) == -1
+
+
+def _view(lib, n=64, k=256, nplanes=8, ptr=FAKE):
+    v = nbw.WView()
+    st = lib.nbw_make_view(ctypes.c_void_p(ptr), n, k, nplanes, ctypes.byref(v))
+    return st, v
+
+
+def test_make_and_slice_view(lib):
+    st, v = _view(lib)
+    assert st == OK and v.nplanes == 8 and v.layout == 1 and v.plane_bytes == 64 * 32
+    c = nbw.WView()
+    assert lib.nbw_slice_view(ctypes.byref(v), 3, ctypes.byref(c)) == OK
+    assert c.planes == v.planes and c.nplanes == 3 and c.plane_bytes == v.plane_bytes
+    c2 = nbw.WView()
+    assert lib.nbw_slice_view(ctypes.byref(c), 4, ctypes.byref(c2)) == ERANGE
+    assert lib.nbw_slice_view(ctypes.byref(v), 0, ctypes.byref(c2)) == ERANGE
+    assert lib.nbw_slice_view(ctypes.byref(v), 9, ctypes.byref(c2)) == ERANGE
+    assert lib.nbw_slice_view(None, 2, ctypes.byref(c2)) == EINVAL
+    assert _view(lib, ptr=FAKE + 8)[0] == EALIGN
+    assert _view(lib, k=200)[0] == EINVAL
+    assert _view(lib, n=0)[0] == EINVAL
+    assert _view(lib, nplanes=0)[0] == ERANGE
+    assert _view(lib, ptr=0)[0] == EINVAL
+
+
+def test_qgemm_validation_before_any_hip_call(lib):
+    _, v = _view(lib)
+    p = ctypes.c_void_p
+    q = lib.nbw_qgemm_kernel
+    args = dict(x=p(FAKE), b=4, s=p(FAKE), r=4, y=p(FAKE), kern=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return q(a["x"], a["b"], ctypes.byref(kw.get("view", v)), a["s"], a["r"], a["y"], a["kern"],
+                 None)
+
+    assert call(x=p(0)) == EINVAL
+    assert call(y=p(0)) == EINVAL
+    assert call(s=p(0)) == EINVAL
+    assert call(b=-1) == EINVAL
+    assert call(r=0) == ERANGE
+    assert call(r=9) == ERANGE
+    assert call(kern=7) == EUNSUPPORTED
+    assert call(x=p(FAKE + 2)) == EALIGN
+    assert call(y=p(FAKE + 4)) == EALIGN
+    assert call(s=p(FAKE + 1)) == EALIGN
+    child = nbw.WView()
+    lib.nbw_slice_view(ctypes.byref(v), 2, ctypes.byref(child))
+    assert call(view=child, r=3) == ERANGE
+    bad = nbw.WView.from_buffer_copy(v)
+    bad.layout = 9
+    assert call(view=bad) == EUNSUPPORTED
+    bad = nbw.WView.from_buffer_copy(v)
+    bad.plane_bytes += 16
+    assert call(view=bad) == EINVAL
+    # the empty product is valid and touches nothing
+    assert call(b=0, x=p(0), y=p(0), s=p(0)) == OK
+
+
+def test_pack_and_unpack_validation(lib):
+    p = ctypes.c_void_p
+    pb = lib.nbw_plane_bytes(64, 256)
+    assert lib.nbw_pack_bitplanes(p(0), 64, 256, p(FAKE), 8 * pb, None) == EINVAL
+    assert lib.nbw_pack_bitplanes(p(FAKE), 64, 256, p(FAKE), 8 * pb - 1, None) == EINVAL
+    assert lib.nbw_pack_bitplanes(p(FAKE), 64, 250, p(FAKE), 8 * pb, None) == EINVAL
+    assert lib.nbw_pack_bitplanes(p(FAKE + 4), 64, 256, p(FAKE), 8 * pb, None) == EALIGN
+    _, v = _view(lib)
+    assert lib.nbw_unpack_codes(ctypes.byref(v), 9, p(FAKE), None) == ERANGE
+    assert lib.nbw_unpack_codes(ctypes.byref(v), 3, p(0), None) == EINVAL
+    assert lib.nbw_unpack_codes(ctypes.byref(v), 3, p(FAKE + 1), None) == EALIGN
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.nbw_status_str(s)
+    assert b"gfx950" in lib.nbw_version()
+    assert lib.nbw_last_hip_error() == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        nbw.pack_bitplanes(torch.zeros((16, 128), dtype=torch.uint8))
