@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip batch 4/16/256 and pack timing")
     ap.add_argument("--copies", type=int, default=0, help="parent copies in the rotation (0 = auto)")
+    ap.add_argument("--b1-kernel", default="auto", help="kernel for the batch-1 step (auto, gemv, smallb)")
     return ap.parse_args()
 
 
@@ -101,31 +102,31 @@ def run_step(nbw, layer, rs, step, xkey, ykey, kernel="auto", events=None, torch
             nbw.qgemm(L[xkey], child, L["s"][c], r, out=L[ykey], kernel=kernel)
 
 
-def timed(torch, nbw, layer, rs, steps, warmup, xkey, ykey):
+def timed(torch, nbw, layer, rs, steps, warmup, xkey, ykey, kernel="auto"):
     for s in range(warmup):
-        run_step(nbw, layer, rs, s, xkey, ykey)
+        run_step(nbw, layer, rs, s, xkey, ykey, kernel=kernel)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for s in range(steps):
-        run_step(nbw, layer, rs, warmup + s, xkey, ykey)
+        run_step(nbw, layer, rs, warmup + s, xkey, ykey, kernel=kernel)
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps  # ms per step
 
 
-def per_launch(torch, nbw, layer, rs, steps, xkey, ykey, batch):
+def per_launch(torch, nbw, layer, rs, steps, xkey, ykey, batch, kernel="auto"):
     """Second timed pass with HIP events around every launch (same stream)."""
     events = []
     for s in range(steps):
-        run_step(nbw, layer, rs, s, xkey, ykey, events=events, torch=torch)
+        run_step(nbw, layer, rs, s, xkey, ykey, kernel=kernel, events=events, torch=torch)
     torch.cuda.synchronize()
     groups = {}
     shapes = {}
     for (L, r, e0, e1) in events:
         ms = e0.elapsed_time(e1)
-        name = nbw.kernel_name(batch, L["n"], L["k"], r)
+        name = nbw.kernel_name(batch, L["n"], L["k"], r, kernel)
         g = groups.setdefault(name, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
         g["ms"] += ms
         g["launches"] += 1
@@ -166,11 +167,11 @@ def main():
 
     # ---- headline: batch 1, r = 4, 3, 2
     bytes_step = sum(r * L["n"] * L["k"] // 8 for r in RS_B1 for L in layer.lin)
-    ms = timed(torch, nbw, layer, RS_B1, args.steps, args.warmup, "x1", "y1")
+    ms = timed(torch, nbw, layer, RS_B1, args.steps, args.warmup, "x1", "y1", args.b1_kernel)
     value = bytes_step / (ms * 1e-3) / 1e9
     log(f"batch 1: {ms * 1e3:.1f} us/step, {value:.1f} GB/s")
 
-    groups, shapes = per_launch(torch, nbw, layer, RS_B1, args.steps, "x1", "y1", 1)
+    groups, shapes = per_launch(torch, nbw, layer, RS_B1, args.steps, "x1", "y1", 1, args.b1_kernel)
     dom_name, dom = max(groups.items(), key=lambda kv: kv[1]["ms"])
     dom_avg_us = dom["ms"] / dom["launches"] * 1e3
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
@@ -195,6 +196,29 @@ def main():
                          "batch": 1, "r": list(RS_B1), "parent_copies": layer.copies,
                          "bytes_per_step": bytes_step},
               "roofline": roofline, "per_shape": per_shape}
+
+    # ---- the same 12 products as 3 grouped dispatches (one per r over the four
+    # linears).  Within a real decoder layer the linears depend on each other,
+    # so this is reported beside the headline, not as it.
+    def grouped_step(step):
+        for ri, r in enumerate(RS_B1):
+            c = (step * len(RS_B1) + ri) % layer.copies
+            nbw.qgemm_grouped([(L["x1"], L["w"][c].slice_view(r), L["s"][c], r) for L in layer.lin],
+                              outs=[L["y1"] for L in layer.lin])
+    for s_ in range(args.warmup):
+        grouped_step(s_)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for s_ in range(args.steps):
+        grouped_step(args.warmup + s_)
+    g1.record()
+    torch.cuda.synchronize()
+    gms = g0.elapsed_time(g1) / args.steps
+    result["grouped"] = {"GBps": round(bytes_step / (gms * 1e-3) / 1e9, 1), "ms_per_step": round(gms, 4),
+                         "dispatches_per_step": len(RS_B1),
+                         "note": "4 linears per dispatch, one dispatch per r; independent products"}
+    log(f"batch 1 grouped: {gms * 1e3:.1f} us/step, {result['grouped']['GBps']} GB/s")
 
     if not args.no_extra:
         # ---- pack (once per checkpoint): 1 byte read + 1 byte written per weight

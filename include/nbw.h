@@ -48,7 +48,7 @@
  *        Y[b][i] = sum_j X[b][j] * w[i][j]   (fp32 accumulation).
  *  - k must be a positive multiple of 128; n >= 1; batch >= 0.
  *
- * Alignment: planes, X and Y 16 bytes; scales 2 bytes; codes 16 bytes.
+ * Alignment: planes, X and Y 16 bytes; scales 4 bytes; codes 16 bytes.
  */
 #ifndef NBW_H
 #define NBW_H
@@ -130,6 +130,28 @@ nbw_status nbw_qgemm(const void *x_bf16, int64_t batch, const nbw_wview *w,
 nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *w,
                             const void *scales_bf16, int32_t r, float *y, nbw_kernel kernel,
                             void *stream);
+
+/* One product of a grouped call: Y = X . dequant_r(W)^T for the r-bit child
+ * of `w`, with the same arguments as nbw_qgemm. */
+typedef struct nbw_problem {
+    const void *x_bf16;      /* [batch][k] */
+    int64_t batch;
+    nbw_wview w;             /* weights (a parent or child view) */
+    const void *scales_bf16; /* [n][k/128] */
+    int32_t r;               /* child width, 1..w.nplanes */
+    float *y;                /* [batch][n] */
+} nbw_problem;
+
+/* Several products queued as few dispatches as possible -- for example the
+ * linears of one decoder layer, each sliced to its own r (MatGPTQ: Accurate
+ * and Efficient Post-Training Matryoshka Quantization, abstract: mixed-
+ * precision execution over heterogeneous per-layer bit-widths).  Results are
+ * those of calling nbw_qgemm on each problem in order on `stream`; since the
+ * problems may run concurrently, no problem's output may overlap another's
+ * inputs or output.  Batch-1 problems run as one grouped launch (up to 32
+ * per launch); others are queued one by one.  Every problem is validated
+ * before anything is queued. */
+nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *stream);
 
 /* Child codes q_r = c >> (8 - r) read back from planes 0..r-1 of `w`, through
  * the same in-register plane decode the qgemm kernels use.  codes_out: device

@@ -44,10 +44,16 @@ class WView(ctypes.Structure):
                 ("plane_bytes", ctypes.c_int64)]
 
 
+class Problem(ctypes.Structure):
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("batch", ctypes.c_int64), ("w", WView),
+                ("scales_bf16", ctypes.c_void_p), ("r", ctypes.c_int32), ("y", ctypes.c_void_p)]
+
+
 _LIB = None
 
 EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
-           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_unpack_codes",
+           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_grouped",
+           "nbw_unpack_codes",
            "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
 
 
@@ -73,6 +79,8 @@ def _lib():
         lib.nbw_qgemm.restype = ctypes.c_int
         lib.nbw_qgemm_kernel.argtypes = [vp, i64, pv, vp, i32, vp, ctypes.c_int, vp]
         lib.nbw_qgemm_kernel.restype = ctypes.c_int
+        lib.nbw_qgemm_grouped.argtypes = [ctypes.POINTER(Problem), i32, vp]
+        lib.nbw_qgemm_grouped.restype = ctypes.c_int
         lib.nbw_unpack_codes.argtypes = [pv, i32, vp, vp]
         lib.nbw_unpack_codes.restype = ctypes.c_int
         lib.nbw_status_str.argtypes = [ctypes.c_int]
@@ -98,6 +106,11 @@ def _check(status: int, what: str) -> None:
 
 
 def _stream(t: torch.Tensor):
+    """The current HIP stream of t's device (the handle only; cheap)."""
+    idx = t.device.index if t.device.index is not None else torch.cuda.current_device()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return ctypes.c_void_p(raw(idx))
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
@@ -206,6 +219,40 @@ def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
     return out
 
 
+def qgemm_grouped(items, outs=None):
+    """Several products in as few dispatches as possible.
+
+    ``items``: sequence of ``(x, w, scales, r)`` as for :func:`qgemm`.  Returns the
+    fp32 outputs (or fills ``outs``).  Batch-1 products run as one grouped launch."""
+    items = list(items)
+    if outs is None:
+        outs = [None] * len(items)
+    arr = (Problem * max(1, len(items)))()
+    results = []
+    for j, ((x, w, scales, r), out) in enumerate(zip(items, outs)):
+        _need(x, "x", torch.bfloat16, 2)
+        _need(scales, "scales", torch.bfloat16, 2)
+        b, k = x.shape
+        if k != w.k or tuple(scales.shape) != (w.n, w.k // 128):
+            raise ValueError(f"problem {j}: shapes of x / scales do not match the weights")
+        if out is None:
+            out = torch.empty((b, w.n), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, "out", torch.float32, 2)
+            if tuple(out.shape) != (b, w.n):
+                raise ValueError(f"problem {j}: out must be [{b}][{w.n}]")
+        arr[j].x_bf16 = x.data_ptr()
+        arr[j].batch = b
+        arr[j].w = w.view
+        arr[j].scales_bf16 = scales.data_ptr()
+        arr[j].r = r
+        arr[j].y = out.data_ptr()
+        results.append(out)
+    if items:
+        _check(_lib().nbw_qgemm_grouped(arr, len(items), _stream(items[0][0])), "nbw_qgemm_grouped")
+    return results
+
+
 def unpack_codes(w: PackedWeight, r: int) -> torch.Tensor:
     """Child codes q_r [n][k] (uint8) decoded on the GPU from planes 0..r-1 (test hook)."""
     out = torch.empty((w.n, w.k), dtype=torch.uint8, device=w.storage.device)
@@ -223,6 +270,6 @@ def version() -> str:
     return _lib().nbw_version().decode()
 
 
-__all__ = ["pack_bitplanes", "slice_view", "qgemm", "unpack_codes", "plane_bytes",
+__all__ = ["pack_bitplanes", "slice_view", "qgemm", "qgemm_grouped", "unpack_codes", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]

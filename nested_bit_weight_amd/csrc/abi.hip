@@ -116,7 +116,7 @@ nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *
     if (kernel < NBW_KERNEL_AUTO || kernel > NBW_KERNEL_GEMM) return NBW_EUNSUPPORTED;
     if (batch == 0) return NBW_OK;  // empty product: nothing to read or write
     if (!x_bf16 || !scales_bf16 || !y) return NBW_EINVAL;
-    if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scales_bf16, 2)) return NBW_EALIGN;
+    if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scales_bf16, 4)) return NBW_EALIGN;
     int cus = 0;
     st = cu_count(&cus);
     if (st != NBW_OK) return st;
@@ -138,6 +138,58 @@ nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *
     default: e = nbw::launch_gemm(r, a, cus, (hipStream_t)stream); break;
     }
     return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *stream) {
+    if (count < 0 || (count > 0 && !problems)) return NBW_EINVAL;
+    // Validate everything before queuing anything.
+    for (int32_t j = 0; j < count; ++j) {
+        const nbw_problem &pr = problems[j];
+        nbw_status st = check_view(&pr.w);
+        if (st != NBW_OK) return st;
+        if (pr.batch < 0) return NBW_EINVAL;
+        if (pr.r < 1 || pr.r > 8 || pr.r > pr.w.nplanes) return NBW_ERANGE;
+        if (pr.batch == 0) continue;
+        if (!pr.x_bf16 || !pr.scales_bf16 || !pr.y) return NBW_EINVAL;
+        if (!aligned(pr.x_bf16, 16) || !aligned(pr.y, 16) || !aligned(pr.scales_bf16, 4))
+            return NBW_EALIGN;
+    }
+    int cus = 0;
+    nbw_status st = cu_count(&cus);
+    if (st != NBW_OK) return st;
+    std::vector<nbw::QgemmArgs> group;
+    std::vector<int> rs;
+    const int cap = nbw::gemv_group_capacity();
+    auto flush = [&]() -> nbw_status {
+        if (group.empty()) return NBW_OK;
+        hipError_t e = nbw::launch_gemv_group(group.data(), rs.data(), (int)group.size(), cus,
+                                              (hipStream_t)stream);
+        group.clear();
+        rs.clear();
+        return e == hipSuccess ? NBW_OK : hip_failed(e);
+    };
+    for (int32_t j = 0; j < count; ++j) {
+        const nbw_problem &pr = problems[j];
+        if (pr.batch == 0) continue;
+        nbw::QgemmArgs a;
+        a.x = (const uint16_t *)pr.x_bf16;
+        a.batch = pr.batch;
+        a.planes = (const uint8_t *)pr.w.planes;
+        a.plane_bytes = pr.w.plane_bytes;
+        a.scales = (const uint16_t *)pr.scales_bf16;
+        a.n = (int)pr.w.n;
+        a.k = (int)pr.w.k;
+        a.y = pr.y;
+        if (nbw::gemv_group_eligible(a)) {
+            group.push_back(a);
+            rs.push_back(pr.r);
+            if ((int)group.size() == cap && (st = flush()) != NBW_OK) return st;
+        } else {
+            st = nbw_qgemm(pr.x_bf16, pr.batch, &pr.w, pr.scales_bf16, pr.r, pr.y, stream);
+            if (st != NBW_OK) return st;
+        }
+    }
+    return flush();
 }
 
 nbw_status nbw_qgemm(const void *x_bf16, int64_t batch, const nbw_wview *w,

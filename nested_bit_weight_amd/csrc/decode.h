@@ -133,13 +133,28 @@ template <int RP, int C> __host__ __device__ constexpr uint32_t pick_offset_pair
     return pick_magic<RP, C>(m);
 }
 
+// A constant held in a vector register.  gfx950 VALU instructions with three
+// operands accept no literal constant and at most one scalar one, so
+// `(z & mask) | magic` with both constants as literals costs two instructions
+// (and + or); with them in VGPRs it is one v_and_or_b32.  The asm has no side
+// effects, so the compiler hoists it out of loops like any constant.
+__host__ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+    return v;
+#else
+    return c;
+#endif
+}
+
 // Phase 2 for one pair.
 template <int RP, int C>
 __host__ __device__ __forceinline__ uint32_t extract(const uint32_t *Z, int m) {
     const Pick p = pick<RP>(m);
     uint32_t z = Z[p.word];
     if (p.shift) z >>= p.shift;
-    return (z & pick_mask<RP>(m)) | pick_magic<RP, C>(m);
+    return (z & vconst(pick_mask<RP>(m))) | vconst(pick_magic<RP, C>(m));
 }
 
 // Decode one 32-column word set of RP planes into 16 bf16 pairs (column pairs
@@ -160,33 +175,51 @@ template <int R> struct Phases {
     static constexpr int c0 = R <= 4 ? 0 : R - 4; // coefficient exponent of phase 0
 };
 
-// Sum over the 16 pairs of one word set of offset_m * (x_lo + x_hi), for both
-// phases: the constant the decoded operands add to sum_k x_k * q_k.
-template <int R>
-__device__ __forceinline__ float offset_dot(const uint32_t *X2, float acc) {
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        uint32_t off = pick_offset_pair<Phases<R>::rp0, Phases<R>::c0>(m);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, off),
-                                              __builtin_bit_cast(bf16x2_t, X2[m]), acc, false);
-        if constexpr (Phases<R>::count == 2) {
-            uint32_t off1 = pick_offset_pair<Phases<R>::rp1, 0>(m);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, off1),
-                                                  __builtin_bit_cast(bf16x2_t, X2[m]), acc,
-                                                  false);
-        }
-    }
-    return acc;
+// Offset classes: the decoded operand of pair m is offset_m + coefficient*q,
+// with offset_m = 2^(C + 7 - lsb_m) per phase, so it depends on m only
+// through (lsb of phase 0, lsb of phase 1) -- a handful of classes.  The
+// correction sum_k x_k * (1/2 - 2^(R-1) - offset_k) therefore needs the pair
+// sums (x_lo + x_hi) collected per class (one dot2 per pair) and one FMA per
+// class, not a product per column.
+template <int R> __host__ __device__ constexpr int lsb0(int m) { return pick<Phases<R>::rp0>(m).lsb; }
+template <int R> __host__ __device__ constexpr int lsb1(int m) {
+    return Phases<R>::rp1 > 0 ? pick<(Phases<R>::rp1 > 0 ? Phases<R>::rp1 : 1)>(m).lsb : 0;
+}
+template <int R> __host__ __device__ constexpr bool class_used(int a, int b) {
+    for (int m = 0; m < 16; ++m)
+        if (lsb0<R>(m) == a && lsb1<R>(m) == b) return true;
+    return false;
 }
 
-// Sum of the 32 x values held as 16 bf16 pairs.
-__device__ __forceinline__ float pair_sum(const uint32_t *X2, float acc) {
+// Correction for NP bf16 pairs (a multiple of 16, pair index mod 16 = m).
+template <int R, int NP>
+__device__ __forceinline__ float correction(const uint32_t *X2) {
+    constexpr int c0 = Phases<R>::c0;
+    float cls[7][7];
+#pragma unroll
+    for (int a = 0; a < 7; ++a)
+#pragma unroll
+        for (int b = 0; b < 7; ++b) cls[a][b] = 0.f;
     const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
-                                              __builtin_bit_cast(bf16x2_t, X2[m]), acc, false);
-    return acc;
+    for (int q = 0; q < NP; ++q) {
+        const int m = q & 15;
+        float &c = cls[lsb0<R>(m)][lsb1<R>(m)];
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
+                                            __builtin_bit_cast(bf16x2_t, X2[q]), c, false);
+    }
+    float corr = 0.f;
+#pragma unroll
+    for (int a = 0; a < 7; ++a)
+#pragma unroll
+        for (int b = 0; b < 7; ++b)
+            if (class_used<R>(a, b)) {
+                float off = (float)(1u << (c0 + 7 - a));
+                if constexpr (Phases<R>::rp1 > 0) off += (float)(1u << (7 - b));
+                const float coef = 0.5f - (float)(1 << (R - 1)) - off;
+                corr = fmaf(coef, cls[a][b], corr);
+            }
+    return corr;
 }
 
 // Decode the r-bit codes of one word set into D0 (phase 0) and D1 (phase 1,

@@ -27,6 +27,13 @@ hipError_t launch_gemv(int r, const QgemmArgs &a, int cu_count, hipStream_t stre
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 
+// Grouped batch-1 launch: several products (each with its own r) as one
+// dispatch.  Eligible problems: batch 1, shapes the streaming kernel takes.
+int gemv_group_capacity();
+bool gemv_group_eligible(const QgemmArgs &a);
+hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
+                             hipStream_t stream);
+
 // Name of the kernel template instance the launcher above would use (as
 // rocprofv3 prints it, without the parameter list).
 void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len);

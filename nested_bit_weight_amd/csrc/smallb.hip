@@ -73,13 +73,9 @@ __global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict_
                 XB[gi][4 * j] = v.x; XB[gi][4 * j + 1] = v.y;
                 XB[gi][4 * j + 2] = v.z; XB[gi][4 * j + 3] = v.w;
             }
-            float o = offset_dot<R>(XB[gi], 0.f);
-            float sx = pair_sum(XB[gi], 0.f);
-            o += __shfl_xor(o, 16);
-            o += __shfl_xor(o, 32);
-            sx += __shfl_xor(sx, 16);
-            sx += __shfl_xor(sx, 32);
-            const float corr = fmaf(0.5f - (float)(1 << (R - 1)), sx, -o);
+            float corr = correction<R, 16>(XB[gi]);
+            corr += __shfl_xor(corr, 16);
+            corr += __shfl_xor(corr, 32);
             init[gi] = f32x4_t{corr, corr, corr, corr};
         }
 

@@ -91,6 +91,7 @@ def test_qgemm_validation_before_any_hip_call(lib):
     assert call(x=p(FAKE + 2)) == EALIGN
     assert call(y=p(FAKE + 4)) == EALIGN
     assert call(s=p(FAKE + 1)) == EALIGN
+    assert call(s=p(FAKE + 2)) == EALIGN
     child = nbw.WView()
     lib.nbw_slice_view(ctypes.byref(v), 2, ctypes.byref(child))
     assert call(view=child, r=3) == ERANGE

@@ -248,6 +248,14 @@ def test_zero_scale_group(nbw):
 
 # ---------------------------------------------------------------- full sizes, sampled
 
+def oracle_rows(d, r, rows):
+    """fp64 oracle for the selected output rows only: the oracle packs just those
+    rows' codes itself (nothing from the GPU)."""
+    sub_codes = np.ascontiguousarray(d["codes"][rows])
+    sub_scales = np.ascontiguousarray(d["scales"][rows])
+    return oracle.qgemm(d["x"], oracle.pack(sub_codes), sub_scales, len(rows), d["k"], r)
+
+
 @pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
 @pytest.mark.parametrize("batch,rs", [(1, (4, 3, 2)), (16, (4, 2)), (256, (8, 4, 3, 2))])
 def test_llama8b_full_size_sampled(nbw, shape_id, batch, rs):
@@ -258,13 +266,74 @@ def test_llama8b_full_size_sampled(nbw, shape_id, batch, rs):
     w = nbw.pack_bitplanes(dev(d["codes"]))
     x = dev(d["x"], torch.bfloat16)
     s = dev(d["scales"], torch.bfloat16)
-    planes = None
     for r in rs:
         y = nbw.qgemm(x, nbw.slice_view(w, r), s, r).cpu().numpy()
-        if planes is None:
-            planes = w.storage.cpu().numpy()
-        ref = oracle.qgemm_rows(d["x"], planes, d["scales"], n, k, r, rows)
-        e = rel_err(y[:, rows], ref)
+        e = rel_err(y[:, rows], oracle_rows(d, r, rows))
         print(f"{d['name']} b={batch} r={r} err={e:.3e}", flush=True)
         assert e <= DESIGN_BOUND
         assert np.all(np.isfinite(y))
+
+
+# ---------------------------------------------------------------- grouped launch
+
+def _grouped_case(nbw, specs, seed):
+    """specs: list of (n, k, batch, r).  Returns items for qgemm_grouped and host data."""
+    items, host = [], []
+    for j, (n, k, b, r) in enumerate(specs):
+        case = synth.random_case(n, k, b, seed=seed + j, recipe="gptq_like", outliers=b > 2)
+        w = nbw.pack_bitplanes(dev(case["codes"]))
+        items.append((dev(case["x"], torch.bfloat16), nbw.slice_view(w, r),
+                      dev(case["scales"], torch.bfloat16), r))
+        host.append((case, r))
+    return items, host
+
+
+def test_grouped_matches_single_launches_and_oracle(nbw):
+    # Mixed shapes (ragged n), mixed widths, one grouped dispatch: bit-identical
+    # to the single-product kernel (same per-row summation order) and within the
+    # design bound of the oracle.
+    specs = [(1000, 1024, 1, 4), (48, 384 + 128, 1, 2), (16, 128 * 6, 1, 8), (333, 2048, 1, 3),
+             (64, 256, 1, 1), (200, 1024, 1, 6)]
+    items, host = _grouped_case(nbw, specs, seed=70)
+    outs = nbw.qgemm_grouped(items)
+    torch.cuda.synchronize()
+    for (x, w, s, r), y, (case, _) in zip(items, outs, host):
+        single = nbw.qgemm(x, w, s, r, kernel="gemv")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), single.cpu().numpy())
+        ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], case["n"],
+                           case["k"], r)
+        assert rel_err(y.cpu().numpy(), ref) <= DESIGN_BOUND
+
+
+def test_grouped_mixed_batches_and_fallbacks(nbw):
+    # batch 0 (no-op), batch 3 (queued on its own), odd k/128 (single-launch kernel)
+    specs = [(100, 512, 1, 4), (64, 384, 1, 3), (70, 512, 3, 2), (32, 256, 0, 5), (50, 1024, 1, 2)]
+    items, host = _grouped_case(nbw, specs, seed=80)
+    outs = nbw.qgemm_grouped(items)
+    torch.cuda.synchronize()
+    for y, (case, r) in zip(outs, host):
+        if case["x"].shape[0] == 0:
+            assert tuple(y.shape) == (0, case["n"])
+            continue
+        ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], case["n"],
+                           case["k"], r)
+        assert rel_err(y.cpu().numpy(), ref) <= DESIGN_BOUND
+
+
+def test_grouped_llama8b_layer_sampled(nbw):
+    # The four Llama-3.1-8B linears at full size, each with its own width.
+    widths = (4, 3, 2, 4)
+    items, ds = [], []
+    for sid, r in enumerate(widths):
+        d = synth.make_linear("llama3.1-8b", sid, 1)
+        w = nbw.pack_bitplanes(dev(d["codes"]))
+        items.append((dev(d["x"], torch.bfloat16), nbw.slice_view(w, r),
+                      dev(d["scales"], torch.bfloat16), r))
+        ds.append(d)
+    outs = nbw.qgemm_grouped(items)
+    torch.cuda.synchronize()
+    for (x, w, s, r), y, d in zip(items, outs, ds):
+        n = d["n"]
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n).integers(0, n, 40)]))
+        assert rel_err(y.cpu().numpy()[:, rows], oracle_rows(d, r, rows)) <= DESIGN_BOUND
