@@ -7,16 +7,22 @@ A step is one pass of the hot path over the Llama-3.1-8B-shaped decoder linears
 X bf16 N(0, 1)) at batch 1: for each child width r in (4, 3, 2), slice the
 parent (host-only view) and run qgemm on all four linears -- 12 launches that
 read r/8 bytes per weight of bit-planes.  ``value`` is plane bytes read per
-second over the timed steps (whole job, inputs resident in HBM).  Packing is
-once per checkpoint and is timed separately (``pack`` field).
+second over the timed steps (whole job, inputs resident in HBM).
+
+A decode step is a chain of short launches, so the step is captured once into a
+HIP graph per parent copy and replayed (``value``); the same step launched from
+Python one call at a time is reported as ``eager``.  Packing is once per
+checkpoint and is timed separately (``pack`` field).
 
 To measure HBM and not the 256 MB MALL, every (step, r) uses its own parent
 copy from a rotation of copies totalling >1.2 GB.
 
-Extra fields: the dominant kernel's roofline (HIP events around every launch
-in a second timed pass), batch 4 and 16 on the same linears, batch 256
-(TFLOP/s, r in 8, 4, 3, 2, activations with 1% outlier channels x10), and the
-CPU oracle timed on this host on the same batch-1 step.
+Extra fields: per-kernel durations (each product replayed back to back in a
+graph over the copy rotation, HIP events around the replays) giving the
+dominant kernel's roofline; the 12 products as 3 grouped dispatches; batch 4
+and 16 on the same linears; batch 256 (TFLOP/s, r in 8, 4, 3, 2, activations
+with 1% outlier channels x10); the CPU oracle timed on this host on a bounded
+sample of the batch-1 step.
 """
 from __future__ import annotations
 
@@ -34,6 +40,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 RS_B1 = (4, 3, 2)
 RS_B256 = (8, 4, 3, 2)
+CPU_SAMPLE_SECONDS = 12.0
 
 
 def log(msg):
@@ -43,8 +50,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip batch 4/16/256 and pack timing")
     ap.add_argument("--copies", type=int, default=0, help="parent copies in the rotation (0 = auto)")
@@ -67,7 +74,7 @@ class Layer:
                              "x1": torch.from_numpy(d["x"]).view(torch.bfloat16).cuda()})
         parent_bytes = sum(8 * L["w"][0].plane_bytes for L in self.lin)
         if copies <= 0:
-            copies = max(3, -(-int(1.2e9) // parent_bytes))
+            copies = max(6, -(-int(1.2e9) // parent_bytes))
         for L in self.lin:
             for _ in range(copies - 1):
                 st = L["w"][0].storage.clone()
@@ -78,64 +85,108 @@ class Layer:
         torch.cuda.synchronize()
 
 
-def launches(layer, rs, step):
-    """(linear, r, copy) for every launch of one step."""
-    out = []
+def copy_of(layer, rs, step, ri):
+    return (step * len(rs) + ri) % layer.copies
+
+
+def step_calls(nbw, layer, rs, step, xkey, ykey, kernel):
+    """Prepared qgemm calls of one step: every r, every linear, in order."""
+    calls = []
     for ri, r in enumerate(rs):
-        c = (step * len(rs) + ri) % layer.copies
+        c = copy_of(layer, rs, step, ri)
         for L in layer.lin:
-            out.append((L, r, c))
+            calls.append(nbw.QgemmCall(L[xkey], L["w"][c].slice_view(r), L["s"][c], r,
+                                       out=L[ykey], kernel=kernel))
+    return calls
+
+
+def capture(torch, fn):
+    """fn() captured into a HIP graph (fn launches on the current stream)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # once eagerly on a side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def event_time(torch, body, steps):
+    """ms per step of body(i) for i in range(steps), HIP events on the current stream."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        body(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+class Stepper:
+    """One step (every r x every linear) as prepared calls and as HIP graphs.
+
+    Step i and step i + copies are the same launches, so one graph per residue
+    modulo the rotation covers every step."""
+
+    def __init__(self, torch, nbw, layer, rs, xkey, ykey, kernel="auto", graphs=True):
+        self.torch = torch
+        self.period = layer.copies
+        self.calls = [step_calls(nbw, layer, rs, j, xkey, ykey, kernel) for j in range(self.period)]
+        self.graphs = None
+        if graphs:
+            self.graphs = [capture(torch, lambda cl=cl: [c() for c in cl]) for cl in self.calls]
+
+    def eager(self, i):
+        for c in self.calls[i % self.period]:
+            c()
+
+    def replay(self, i):
+        self.graphs[i % self.period].replay()
+
+    def time(self, steps, warmup, graph=True):
+        body = self.replay if graph else self.eager
+        for i in range(warmup):
+            body(i)
+        return event_time(self.torch, lambda i: body(warmup + i), steps)
+
+
+def kernel_durations(torch, nbw, layer, rs, xkey, ykey, batch, kernel, reps):
+    """Back-to-back duration of every product of the step.
+
+    For each (linear, r) a graph holds that product once per parent copy (so no
+    launch re-reads what the previous one left in cache); the graph is replayed
+    ``reps`` times between two HIP events.  Returns {(linear, r): us per launch}."""
+    out = {}
+    for r in rs:
+        for L in layer.lin:
+            calls = [nbw.QgemmCall(L[xkey], L["w"][c].slice_view(r), L["s"][c], r, out=L[ykey],
+                                   kernel=kernel) for c in range(layer.copies)]
+            g = capture(torch, lambda cl=calls: [c() for c in cl])
+            g.replay()
+            ms = event_time(torch, lambda i: g.replay(), reps)
+            out[(L["name"], r)] = {"us": ms * 1e3 / len(calls), "n": L["n"], "k": L["k"],
+                                   "kernel": nbw.kernel_name(batch, L["n"], L["k"], r, kernel)}
+            del g
     return out
 
 
-def run_step(nbw, layer, rs, step, xkey, ykey, kernel="auto", events=None, torch=None):
-    for (L, r, c) in launches(layer, rs, step):
-        child = L["w"][c].slice_view(r)
-        if events is not None:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            nbw.qgemm(L[xkey], child, L["s"][c], r, out=L[ykey], kernel=kernel)
-            e1.record()
-            events.append((L, r, e0, e1))
-        else:
-            nbw.qgemm(L[xkey], child, L["s"][c], r, out=L[ykey], kernel=kernel)
-
-
-def timed(torch, nbw, layer, rs, steps, warmup, xkey, ykey, kernel="auto"):
-    for s in range(warmup):
-        run_step(nbw, layer, rs, s, xkey, ykey, kernel=kernel)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for s in range(steps):
-        run_step(nbw, layer, rs, warmup + s, xkey, ykey, kernel=kernel)
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps  # ms per step
-
-
-def per_launch(torch, nbw, layer, rs, steps, xkey, ykey, batch, kernel="auto"):
-    """Second timed pass with HIP events around every launch (same stream)."""
-    events = []
-    for s in range(steps):
-        run_step(nbw, layer, rs, s, xkey, ykey, kernel=kernel, events=events, torch=torch)
-    torch.cuda.synchronize()
-    groups = {}
-    shapes = {}
-    for (L, r, e0, e1) in events:
-        ms = e0.elapsed_time(e1)
-        name = nbw.kernel_name(batch, L["n"], L["k"], r, kernel)
-        g = groups.setdefault(name, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
-        g["ms"] += ms
-        g["launches"] += 1
-        g["bytes"] += r * L["n"] * L["k"] // 8
-        g["flops"] += 2 * batch * L["n"] * L["k"]
-        sh = shapes.setdefault((L["name"], r), [0.0, 0])
-        sh[0] += ms
-        sh[1] += 1
-    return groups, shapes
+def dominant(durs, batch):
+    """Kernel with the largest total time in one step, and its launches' totals."""
+    tot = {}
+    for (nm, r), d in durs.items():
+        t = tot.setdefault(d["kernel"], {"us": 0.0, "launches": 0, "bytes": 0, "flops": 0})
+        t["us"] += d["us"]
+        t["launches"] += 1
+        t["bytes"] += r * d["n"] * d["k"] // 8
+        t["flops"] += 2 * batch * d["n"] * d["k"]
+    name, t = max(tot.items(), key=lambda kv: kv[1]["us"])
+    return name, t
 
 
 def main():
@@ -165,57 +216,62 @@ def main():
     for L in layer.lin:
         L["y1"] = torch.empty((1, L["n"]), dtype=torch.float32, device="cuda")
 
-    # ---- headline: batch 1, r = 4, 3, 2
+    # ---- headline: batch 1, r = 4, 3, 2, the step replayed as a HIP graph
     bytes_step = sum(r * L["n"] * L["k"] // 8 for r in RS_B1 for L in layer.lin)
-    ms = timed(torch, nbw, layer, RS_B1, args.steps, args.warmup, "x1", "y1", args.b1_kernel)
+    st1 = Stepper(torch, nbw, layer, RS_B1, "x1", "y1", args.b1_kernel)
+    ms = st1.time(args.steps, args.warmup, graph=True)
     value = bytes_step / (ms * 1e-3) / 1e9
-    log(f"batch 1: {ms * 1e3:.1f} us/step, {value:.1f} GB/s")
+    log(f"batch 1 (graph): {ms * 1e3:.1f} us/step, {value:.1f} GB/s")
+    ms_eager = st1.time(args.steps, args.warmup, graph=False)
+    log(f"batch 1 (eager): {ms_eager * 1e3:.1f} us/step, {bytes_step / (ms_eager * 1e-3) / 1e9:.1f} GB/s")
+    del st1
 
-    groups, shapes = per_launch(torch, nbw, layer, RS_B1, args.steps, "x1", "y1", 1, args.b1_kernel)
-    dom_name, dom = max(groups.items(), key=lambda kv: kv[1]["ms"])
-    dom_avg_us = dom["ms"] / dom["launches"] * 1e3
-    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    durs = kernel_durations(torch, nbw, layer, RS_B1, "x1", "y1", 1, args.b1_kernel,
+                            reps=max(10, args.steps // 4))
+    dom_name, dom = dominant(durs, 1)
+    dom_avg_us = dom["us"] / dom["launches"]
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": dom_name, "avg_launch_us": round(dom_avg_us, 2),
-                "bytes_per_launch": dom["bytes"] // dom["launches"]}
-    size = {L["name"]: L["n"] * L["k"] for L in layer.lin}
-    per_shape = []
-    for (nm, r), (tot_ms, cnt) in sorted(shapes.items()):
-        us = tot_ms / cnt * 1e3
-        per_shape.append({"linear": nm, "r": r, "us": round(us, 2),
-                          "GBps": round(r * size[nm] / 8 / (us * 1e-6) / 1e9, 1)})
+                "bytes_per_launch": dom["bytes"] // dom["launches"],
+                "launches_per_step": dom["launches"]}
+    per_shape = [{"linear": nm, "r": r, "us": round(d["us"], 2),
+                  "GBps": round(r * d["n"] * d["k"] / 8 / (d["us"] * 1e-6) / 1e9, 1),
+                  "kernel": d["kernel"]}
+                 for (nm, r), d in sorted(durs.items())]
     log(f"dominant kernel {dom_name}: {dom_avg_us:.2f} us avg, {achieved:.1f} GB/s")
+    for p in per_shape:
+        log(f"  {p['linear']:8s} r={p['r']} {p['us']:7.2f} us {p['GBps']:7.1f} GB/s  {p['kernel']}")
 
     result = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-              "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+              "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
               "data": "synthetic",
               "config": {"workload": "llama3.1-8b decoder linears qkv/o/gate_up/down, batch 1, "
-                                     "r=4,3,2 (12 qgemm launches per step)",
+                                     "r=4,3,2 (12 qgemm launches per step, HIP graph replay)",
                          "batch": 1, "r": list(RS_B1), "parent_copies": layer.copies,
                          "bytes_per_step": bytes_step},
-              "roofline": roofline, "per_shape": per_shape}
+              "roofline": roofline,
+              "eager": {"GBps": round(bytes_step / (ms_eager * 1e-3) / 1e9, 1),
+                        "ms_per_step": round(ms_eager, 5),
+                        "note": "same step, one Python call per launch, no graph"},
+              "per_shape": per_shape}
 
     # ---- the same 12 products as 3 grouped dispatches (one per r over the four
     # linears).  Within a real decoder layer the linears depend on each other,
     # so this is reported beside the headline, not as it.
     def grouped_step(step):
         for ri, r in enumerate(RS_B1):
-            c = (step * len(RS_B1) + ri) % layer.copies
+            c = copy_of(layer, RS_B1, step, ri)
             nbw.qgemm_grouped([(L["x1"], L["w"][c].slice_view(r), L["s"][c], r) for L in layer.lin],
                               outs=[L["y1"] for L in layer.lin])
-    for s_ in range(args.warmup):
-        grouped_step(s_)
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record()
-    for s_ in range(args.steps):
-        grouped_step(args.warmup + s_)
-    g1.record()
-    torch.cuda.synchronize()
-    gms = g0.elapsed_time(g1) / args.steps
-    result["grouped"] = {"GBps": round(bytes_step / (gms * 1e-3) / 1e9, 1), "ms_per_step": round(gms, 4),
+    ggraphs = [capture(torch, lambda j=j: grouped_step(j)) for j in range(layer.copies)]
+    for i in range(args.warmup):
+        ggraphs[i % layer.copies].replay()
+    gms = event_time(torch, lambda i: ggraphs[(args.warmup + i) % layer.copies].replay(), args.steps)
+    del ggraphs
+    result["grouped"] = {"GBps": round(bytes_step / (gms * 1e-3) / 1e9, 1), "ms_per_step": round(gms, 5),
                          "dispatches_per_step": len(RS_B1),
                          "note": "4 linears per dispatch, one dispatch per r; independent products"}
     log(f"batch 1 grouped: {gms * 1e3:.1f} us/step, {result['grouped']['GBps']} GB/s")
@@ -227,17 +283,12 @@ def main():
         outs = [torch.empty(8 * L["w"][0].plane_bytes, dtype=torch.uint8, device="cuda") for L in L0]
         for c, o in zip(codes, outs):
             nbw.pack_bitplanes(c, out=o)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 5
-        e0.record()
-        for _ in range(reps):
+
+        def pack_all(_):
             for c, o in zip(codes, outs):
                 nbw.pack_bitplanes(c, out=o)
-        e1.record()
-        torch.cuda.synchronize()
-        pack_bytes = reps * sum(2 * L["n"] * L["k"] for L in L0)
-        pack_gbs = pack_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        pms = event_time(torch, pack_all, 5)
+        pack_gbs = sum(2 * L["n"] * L["k"] for L in L0) / (pms * 1e-3) / 1e9
         result["pack"] = {"GBps": round(pack_gbs, 1), "frac_hbm": round(pack_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_weight": 2}
         del codes, outs
@@ -245,39 +296,46 @@ def main():
 
         # ---- batch 4 and 16 (same linears, same recipe)
         other = {}
+        wid = synth.WORKLOAD_IDS["llama3.1-8b"]
         for b in (4, 16):
-            wid = synth.WORKLOAD_IDS["llama3.1-8b"]
             for sid, L in enumerate(layer.lin):
                 xb = synth.activations(b, L["k"], synth.rng_for(0, wid, sid, synth.T_X))
                 L[f"x{b}"] = torch.from_numpy(xb).view(torch.bfloat16).cuda()
                 L[f"y{b}"] = torch.empty((b, L["n"]), dtype=torch.float32, device="cuda")
-            msb = timed(torch, nbw, layer, RS_B1, max(5, args.steps // 2), 2, f"x{b}", f"y{b}")
+            stb = Stepper(torch, nbw, layer, RS_B1, f"x{b}", f"y{b}")
+            msb = stb.time(max(10, args.steps // 4), 5, graph=True)
+            del stb
             other[f"batch{b}"] = {"GBps": round(bytes_step / (msb * 1e-3) / 1e9, 1),
-                                  "ms_per_step": round(msb, 4)}
+                                  "ms_per_step": round(msb, 5)}
             log(f"batch {b}: {other[f'batch{b}']['GBps']} GB/s")
         result["other_batches"] = other
 
         # ---- batch 256, r = 8, 4, 3, 2: TFLOP/s
         B = 256
-        wid = synth.WORKLOAD_IDS["llama3.1-8b"]
         for sid, L in enumerate(layer.lin):
             d = synth.activations(B, L["k"], synth.rng_for(0, wid, sid, synth.T_X), outliers=True,
                                   outlier_rng=synth.rng_for(0, wid, sid, synth.T_OUTLIERS))
             L["x256"] = torch.from_numpy(d).view(torch.bfloat16).cuda()
             L["y256"] = torch.empty((B, L["n"]), dtype=torch.float32, device="cuda")
         flops_step = sum(2 * B * L["n"] * L["k"] for _ in RS_B256 for L in layer.lin)
-        ms256 = timed(torch, nbw, layer, RS_B256, 3, 1, "x256", "y256")
+        st256 = Stepper(torch, nbw, layer, RS_B256, "x256", "y256")
+        ms256 = st256.time(max(4, args.steps // 20), 2, graph=True)
+        del st256
         tflops = flops_step / (ms256 * 1e-3) / 1e12
-        g256, _ = per_launch(torch, nbw, layer, RS_B256, 2, "x256", "y256", B)
-        n256, d256 = max(g256.items(), key=lambda kv: kv[1]["ms"])
-        ach256 = d256["flops"] / (d256["ms"] * 1e-3) / 1e12
-        result["batch256"] = {"TFLOPs": round(tflops, 2), "ms_per_step": round(ms256, 4),
+        d256 = kernel_durations(torch, nbw, layer, RS_B256, "x256", "y256", B, "auto", reps=3)
+        n256, t256 = dominant(d256, B)
+        ach256 = t256["flops"] / (t256["us"] * 1e-6) / 1e12
+        result["batch256"] = {"TFLOPs": round(tflops, 2), "ms_per_step": round(ms256, 5),
                               "r": list(RS_B256),
                               "roofline": {"bound": "mfma", "achieved": round(ach256, 2),
                                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": round(ach256 / BF16_PEAK_TFLOPS, 4),
                                            "kernel": n256,
-                                           "avg_launch_us": round(d256["ms"] / d256["launches"] * 1e3, 2)}}
+                                           "avg_launch_us": round(t256["us"] / t256["launches"], 2)},
+                              "per_shape": [{"linear": nm, "r": r, "us": round(d["us"], 2),
+                                             "TFLOPs": round(2 * B * d["n"] * d["k"] / (d["us"] * 1e-6)
+                                                             / 1e12, 1)}
+                                            for (nm, r), d in sorted(d256.items())]}
         log(f"batch 256: {tflops:.1f} TFLOP/s; {n256} {ach256:.1f} TFLOP/s")
 
     if not args.no_cpu_baseline:
@@ -287,9 +345,10 @@ def main():
 
 
 def cpu_baseline(synth):
-    """The CPU oracle, as it stands, on the same batch-1 step (all 12 products)."""
-    import numpy as np
+    """The CPU oracle, as it stands, on a bounded sample of the batch-1 step.
 
+    Whole steps (all 12 products) are repeated until CPU_SAMPLE_SECONDS have
+    passed; the rate is plane bytes of the completed steps over their time."""
     import oracle
 
     wl = "llama3.1-8b"
@@ -299,17 +358,22 @@ def cpu_baseline(synth):
         ins.append((d, oracle.pack(d["codes"])))
     t0 = time.time()
     total = 0
-    for r in RS_B1:
-        for d, planes in ins:
-            oracle.qgemm(d["x"], planes, d["scales"], d["n"], d["k"], r)
-            total += r * d["n"] * d["k"] // 8
+    steps = 0
+    while True:
+        for r in RS_B1:
+            for d, planes in ins:
+                oracle.qgemm(d["x"], planes, d["scales"], d["n"], d["k"], r)
+                total += r * d["n"] * d["k"] // 8
+        steps += 1
+        if time.time() - t0 >= CPU_SAMPLE_SECONDS:
+            break
     dt = time.time() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    log(f"cpu oracle: {dt:.1f} s, {total / dt / 1e9:.3f} GB/s on {cores} threads")
+    log(f"cpu oracle: {steps} steps in {dt:.1f} s, {total / dt / 1e9:.3f} GB/s on {cores} threads")
     return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": "the full batch-1 step: 4 Llama-3.1-8B linears x r=4,3,2, fp64 oracle "
-                      "(oracle/nbw_oracle.c, OpenMP over output rows)"}
+            "seconds": round(dt, 2), "steps": steps,
+            "sample": f"{steps} whole batch-1 steps (4 Llama-3.1-8B linears x r=4,3,2 each), "
+                      "fp64 oracle (oracle/nbw_oracle.c, OpenMP over output rows)"}
 
 
 if __name__ == "__main__":

@@ -105,13 +105,18 @@ def _check(status: int, what: str) -> None:
         raise NBWError(status, what)
 
 
+def _raw_stream(device_index: int) -> int:
+    """Raw handle of the current HIP stream of a device."""
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device_index)
+    return torch.cuda.current_stream(device_index).cuda_stream
+
+
 def _stream(t: torch.Tensor):
     """The current HIP stream of t's device (the handle only; cheap)."""
     idx = t.device.index if t.device.index is not None else torch.cuda.current_device()
-    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if raw is not None:
-        return ctypes.c_void_p(raw(idx))
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(_raw_stream(idx))
 
 
 def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
@@ -219,6 +224,51 @@ def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
     return out
 
 
+class QgemmCall:
+    """One qgemm with its arguments checked and marshalled once.
+
+    Calling it issues the product on the current stream of the inputs' device (or on
+    ``stream``, a raw HIP stream handle) with a single library call; the tensors are
+    kept alive by the object.  Use it where per-call Python cost matters, e.g. when a
+    decode step is captured into a HIP graph or launched in a tight loop."""
+
+    __slots__ = ("x", "w", "scales", "r", "out", "kernel", "_args", "_fn", "_dev")
+
+    def __init__(self, x, w, scales, r, out=None, kernel="auto"):
+        _need(x, "x", torch.bfloat16, 2)
+        _need(scales, "scales", torch.bfloat16, 2)
+        b, k = x.shape
+        if k != w.k:
+            raise ValueError(f"x has k={k}, weights have k={w.k}")
+        if tuple(scales.shape) != (w.n, w.k // 128):
+            raise ValueError(f"scales must be [{w.n}][{w.k // 128}], got {tuple(scales.shape)}")
+        if scales.device != x.device or w.storage.device != x.device:
+            raise ValueError("x, scales and weights must be on the same GPU")
+        if out is None:
+            out = torch.empty((b, w.n), dtype=torch.float32, device=x.device)
+        else:
+            _need(out, "out", torch.float32, 2)
+            if tuple(out.shape) != (b, w.n) or out.device != x.device:
+                raise ValueError(f"out must be [{b}][{w.n}] on the same GPU")
+        if kernel not in KERNELS:
+            raise ValueError(f"unknown kernel {kernel!r}")
+        self.x, self.w, self.scales, self.r, self.out, self.kernel = x, w, scales, r, out, kernel
+        view = WView.from_buffer_copy(w.view)  # byref() below keeps it alive
+        self._args = (ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(view),
+                      ctypes.c_void_p(scales.data_ptr()), r, ctypes.c_void_p(out.data_ptr()),
+                      KERNELS[kernel])
+        self._fn = _lib().nbw_qgemm_kernel
+        self._dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+
+    def __call__(self, stream=None):
+        if stream is None:
+            stream = _raw_stream(self._dev)
+        st = self._fn(*self._args, ctypes.c_void_p(stream))
+        if st != 0:
+            raise NBWError(st, "nbw_qgemm")
+        return self.out
+
+
 def qgemm_grouped(items, outs=None):
     """Several products in as few dispatches as possible.
 
@@ -270,6 +320,6 @@ def version() -> str:
     return _lib().nbw_version().decode()
 
 
-__all__ = ["pack_bitplanes", "slice_view", "qgemm", "qgemm_grouped", "unpack_codes", "plane_bytes",
+__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "unpack_codes", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]

@@ -191,6 +191,14 @@ template <int R> __host__ __device__ constexpr bool class_used(int a, int b) {
     return false;
 }
 
+// Coefficient of the pair sum (x_2m + x_2m+1) in the correction of pair m:
+// the exact operand is q + 1/2 - 2^(R-1), the decoded one offset_m + q.
+template <int R> __host__ __device__ constexpr float pair_coef(int m) {
+    float off = (float)(1u << (Phases<R>::c0 + 7 - lsb0<R>(m)));
+    if (Phases<R>::rp1 > 0) off += (float)(1u << (7 - lsb1<R>(m)));
+    return 0.5f - (float)(1 << (R - 1)) - off;
+}
+
 // Correction for NP bf16 pairs (a multiple of 16, pair index mod 16 = m).
 template <int R, int NP>
 __device__ __forceinline__ float correction(const uint32_t *X2) {

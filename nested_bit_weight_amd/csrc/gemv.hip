@@ -35,19 +35,23 @@
 
 namespace nbw {
 
-constexpr int GEMV_WAVES = 4;       // waves per workgroup: two workgroups share a CU
+constexpr int GEMV_MAX_WAVES = 8;   // waves per workgroup (the launch picks 4 or 8)
+constexpr int GEMV_ODD_WAVES = 4;   // waves per workgroup of the odd-group-count kernel
 constexpr int GEMV_MAX_TILES = 16;  // tiles per workgroup
 constexpr int GEMV_MAX_GROUP = 32;  // products per grouped launch
 
-// Steps of planes a wave keeps in flight: about 16 x 16-byte loads per lane.
-__host__ __device__ constexpr int gemv_depth(int r) {
-    return r <= 2 ? 8 : (r == 3 ? 5 : (r == 4 ? 4 : 2));
-}
+// Steps a wave keeps in flight (prefetch depth).  Every wave of the grid
+// prefetches this many steps at once, so the total in flight must stay near
+// what HBM delivers in one memory latency, not a large share of the matrix:
+// a deeper queue only delays each wave's first step.  Waves with only a few
+// steps take depth 1 (a second buffer would hold repeats of the last step).
+constexpr int GEMV_DEPTH_SHORT = 1;
+__host__ __device__ constexpr int gemv_depth(int r) { return r <= 4 ? 2 : 1; }
 
-// Dynamic LDS: X bf16 [k] | corr fp32 [k/128] | per-lane partial sums fp32
-// [W][GEMV_MAX_TILES][64].
-__host__ __device__ constexpr size_t gemv_lds_bytes(int k, int waves) {
-    return (size_t)k * 2 + (size_t)(k / 128) * 4 + (size_t)waves * GEMV_MAX_TILES * 64 * 4;
+// Dynamic LDS: per wave, one set of X (4 groups x 128 bf16 = 1 KB), then the
+// per-lane partial sums fp32 [W][slots][64], one slot per tile.
+__host__ __device__ constexpr size_t gemv_lds_bytes(int waves, int slots) {
+    return (size_t)waves * 1024 + (size_t)waves * slots * 64 * 4;
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -55,13 +59,20 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// One workgroup: tiles [t_begin, t_begin + T) of one product, all of k.
+// One workgroup: tiles [t_begin, t_begin + T) of one product, all of k;
+// `slots` partial-sum slots per wave in LDS (T <= slots).
+//
+// Waves are independent until the final reduction: a wave loads the X of its
+// current set itself (one 16-byte load per lane, part of the step's load
+// stream), stages it in its own 1 KB of LDS and reads back its lanes'
+// groups, so no barrier -- and no wait for every load in flight -- stands
+// between a wave's first loads and its first step.
 template <int R, int PD>
 __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
                                            const uint8_t *__restrict__ planes,
                                            int64_t plane_bytes,
                                            const uint16_t *__restrict__ scales, int n, int k,
-                                           int t_begin, int T, float *__restrict__ y,
+                                           int t_begin, int T, int slots, float *__restrict__ y,
                                            unsigned char *lds) {
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
@@ -69,36 +80,53 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int i = lane & 15, gg = lane >> 4;
-    uint32_t *xs = reinterpret_cast<uint32_t *>(lds);                  // [k/2] bf16 pairs
-    float *corr = reinterpret_cast<float *>(lds + (size_t)k * 2);      // [G]
-    float *red = corr + G;                                             // [W][GEMV_MAX_TILES][64]
+    uint32_t *xw = reinterpret_cast<uint32_t *>(lds) + w * 256;          // this wave's set of X
+    float *red = reinterpret_cast<float *>(lds + (size_t)W * 1024);      // [W][slots][64]
 
     // This wave's (set, tile) steps: set ordinal s = 0 .. my_sets-1 is set
     // w + s*W, tile t = 0 .. T-1; step u = s*T + t.
     const int my_sets = nsets > w ? (nsets - w + W - 1) / W : 0;
     const int U = my_sets * T;
 
-    // 1. Prefetch the first PD steps (planes + the scale word of each).
+    // Zero this wave's partial sums (only this wave writes them until the
+    // final barrier).
+    for (int t = 0; t < T; ++t) red[(w * slots + t) * 64 + lane] = 0.f;
+
+    // Coefficient of this lane's pair sums in the group correction
+    // sum_k x_k * (1/2 - 2^(R-1) - offset_k): lane (i, gg) takes the pairs
+    // i, i+16, i+32, i+48 of its group, which share one offset.
+    float my_coef = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        if (i == m) my_coef = pair_coef<R>(m);
+
+    // Step loads: R plane chunks, the aligned 32-bit scale word, and the
+    // lane's 16 bytes of the set's X (the same chunk for every tile of a set;
+    // reloading it keeps the number of loads per step fixed).  All loads are
+    // unconditional (clamped at the end), so the loads-in-flight count between
+    // a load and its use is static.
     u32x4_t buf[PD][R];
+    u32x4_t xbuf[PD];
     uint32_t sbuf[PD];
     int ps = 0, pt = 0;  // next step to prefetch
+    const int xchunks = k >> 3;
     auto load_step = [&](int j) {
-        // clamped to the last step: past the end the load repeats it (L2 hit)
         int s = ps, t = pt;
         if (s >= my_sets) {
             s = my_sets - 1;
             t = T - 1;
         }
-        const int g = min(4 * (w + s * W) + gg, G - 1);
+        const int set = w + s * W;
+        xbuf[j] = reinterpret_cast<const u32x4_t *>(x)[min(set * 64 + lane, xchunks - 1)];
+        const int g = min(4 * set + gg, G - 1);
         const uint8_t *c = planes + (((int64_t)(t_begin + t) * G + g) * 16 + i) * 16;
 #pragma unroll
         for (int p = 0; p < R; ++p)
             buf[j][p] =
                 __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(c + p * plane_bytes));
-        // The aligned 32-bit word holding this lane's bf16 scale (in bounds:
-        // the host sends only even group counts here).  A 16-bit load would
-        // need a zero-extension that the compiler may put where it waits for
-        // every load in flight.
+        // (in bounds: the host sends only even group counts here; a 16-bit
+        // load would need a zero-extension that the compiler may place where
+        // it waits for every load in flight)
         const int row = min(16 * (t_begin + t) + i, n - 1);
         const int64_t idx = (int64_t)row * G + g;
         sbuf[j] = *reinterpret_cast<const uint32_t *>(scales + (idx & ~(int64_t)1));
@@ -112,37 +140,32 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         for (int j = 0; j < PD; ++j) load_step(j);
     }
 
-    // 2. Stage X in LDS and compute the per-group corrections
-    //    sum_k x_k * (1/2 - 2^(R-1) - offset_k); zero the partial sums.
-    for (int g = threadIdx.x; g < G; g += blockDim.x) {
-        uint32_t X2[64];
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + 128 * g);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const u32x4_t v = src[q];
-            X2[4 * q] = v.x; X2[4 * q + 1] = v.y; X2[4 * q + 2] = v.z; X2[4 * q + 3] = v.w;
-            reinterpret_cast<u32x4_t *>(xs + 64 * g)[q] = v;
-        }
-        corr[g] = correction<R, 64>(X2);
-    }
-    for (int t = 0; t < T; ++t) red[(w * GEMV_MAX_TILES + t) * 64 + lane] = 0.f;
-    __syncthreads();
-
-    // 3. Stream the steps.
     uint32_t X2[64];
     float cg = 0.f;
     int cs = 0, ct = 0;  // step being computed
     auto compute = [&](int j) {
         const int g = 4 * (w + cs * W) + gg;
         const bool gvalid = g < G;
-        if (ct == 0) {  // new set: this lane's activations and correction from LDS
-            const int gc = gvalid ? g : G - 1;
+        if (ct == 0) {
+            // New set: stage its X (LDS operations of one wave complete in
+            // order, so the previous set's reads are done), read back this
+            // lane's group, and form the group's correction over the quarter.
+            reinterpret_cast<u32x4_t *>(xw)[lane] = xbuf[j];
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const u32x4_t v = reinterpret_cast<const u32x4_t *>(xs + 64 * gc)[q];
+                const u32x4_t v = reinterpret_cast<const u32x4_t *>(xw + 64 * gg)[q];
                 X2[4 * q] = v.x; X2[4 * q + 1] = v.y; X2[4 * q + 2] = v.z; X2[4 * q + 3] = v.w;
             }
-            cg = corr[gc];
+            const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
+            float sx = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sx = dot2(one, xw[64 * gg + i + 16 * q], sx);
+            float v = my_coef * sx;
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            cg = v;
         }
         // four independent dot2 chains (one per 32-column word) keep a wave's
         // dependent-issue latency off the critical path
@@ -172,7 +195,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     // returns nothing, so the wave does not wait for it.  Each slot has a
     // single writer, so the order of the additions is fixed.
     auto commit = [&](float v) {
-        __hip_atomic_fetch_add(&red[(w * GEMV_MAX_TILES + ct) * 64 + lane], v,
+        __hip_atomic_fetch_add(&red[(w * slots + ct) * 64 + lane], v,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (++ct == T) {
             ct = 0;
@@ -196,14 +219,14 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     for (int j = 0; j < PD; ++j)  // the last < PD steps are already loaded
         if (Ufull + j < U) commit(compute(j));
 
-    // 4. Rows: add the four groups of each set and the waves, in a fixed order.
+    // Rows: add the four groups of each set and the waves, in a fixed order.
     __syncthreads();
     const float post = (float)(1 << (8 - R));
     for (int e = threadIdx.x; e < T * 16; e += blockDim.x) {
         const int t = e >> 4, ii = e & 15;
         float sum = 0.f;
         for (int ww = 0; ww < W; ++ww) {
-            const float *slot = red + (ww * GEMV_MAX_TILES + t) * 64 + ii;
+            const float *slot = red + (ww * slots + t) * 64 + ii;
             sum += (slot[0] + slot[16]) + (slot[32] + slot[48]);
         }
         const int row = 16 * t_begin + e;
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
                                                        int64_t plane_bytes,
                                                        const uint16_t *__restrict__ scales,
                                                        int n, int k, float *__restrict__ y) {
-    __shared__ float red[GEMV_WAVES][16];
+    __shared__ float red[GEMV_ODD_WAVES][16];
     const int G = k >> 7;
     const int W = blockDim.x >> 6;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -272,17 +295,18 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
     }
 }
 
-template <int R>
-__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t *__restrict__ x,
-                                                   const uint8_t *__restrict__ planes,
-                                                   int64_t plane_bytes,
-                                                   const uint16_t *__restrict__ scales, int n,
-                                                   int k, int tiles_total, int tiles_per_wg,
-                                                   float *__restrict__ y) {
+template <int R, int PD>
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(const uint16_t *__restrict__ x,
+                                                                  const uint8_t *__restrict__ planes,
+                                                                  int64_t plane_bytes,
+                                                                  const uint16_t *__restrict__ scales,
+                                                                  int n, int k, int tiles_total,
+                                                                  int tiles_per_wg,
+                                                                  float *__restrict__ y) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int t_begin = blockIdx.x * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    gemv_tiles<R, gemv_depth(R)>(x, planes, plane_bytes, scales, n, k, t_begin, T, y, lds);
+    gemv_tiles<R, PD>(x, planes, plane_bytes, scales, n, k, t_begin, T, tiles_per_wg, y, lds);
 }
 
 // ---------------------------------------------------------------- grouped launch
@@ -298,11 +322,12 @@ struct GemvJob {
 
 struct GemvGroup {
     GemvJob job[GEMV_MAX_GROUP];
-    int count;
+    int count, slots;
 };
 
-// Workgroup b runs item b; items are numbered product by product.
-__global__ __launch_bounds__(256) void gemv_group_kernel(GemvGroup grp) {
+// Workgroup b runs item b; items are numbered product by product.  Every
+// item has `slots` partial-sum slots per wave (the largest tpw of the group).
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_group_kernel(GemvGroup grp) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int item = blockIdx.x;
     int jb = 0;
@@ -311,10 +336,10 @@ __global__ __launch_bounds__(256) void gemv_group_kernel(GemvGroup grp) {
     const int t_begin = (item - J.item_begin) * J.tpw;
     const int T = min(J.tpw, J.tiles - t_begin);
     switch (J.r) {
-#define NBW_GEMV_CASE(RR)                                                                        \
-    case RR:                                                                                     \
+#define NBW_GEMV_CASE(RR)                                                                    \
+    case RR:                                                                                 \
         gemv_tiles<RR, gemv_depth(RR)>(J.x, J.planes, J.plane_bytes, J.scales, J.n, J.k, t_begin, \
-                                       T, J.y, lds);                                             \
+                                       T, grp.slots, J.y, lds);                              \
         break;
         NBW_GEMV_CASE(1)
         NBW_GEMV_CASE(2)
@@ -330,23 +355,27 @@ __global__ __launch_bounds__(256) void gemv_group_kernel(GemvGroup grp) {
 
 // ---------------------------------------------------------------- host side
 
-// Tiles per workgroup: items of about `target` plane bytes (large enough to
-// amortise a workgroup's start-up, small enough to spread over the CUs),
-// at most GEMV_MAX_TILES, and never fewer workgroups than CUs when the
-// matrix allows it.
-static int gemv_tpw(int n, int k, int r, int cu_count, int64_t target) {
-    const int tiles = (n + 15) / 16;
-    const int64_t tile_bytes = (int64_t)2 * k * r;  // 16 rows x k/8 bytes x r planes
-    int tpw = (int)((target + tile_bytes / 2) / tile_bytes);
-    if (tpw < 1) tpw = 1;
-    if (tpw > GEMV_MAX_TILES) tpw = GEMV_MAX_TILES;
-    const int fill = (tiles + cu_count - 1) / cu_count;  // tiles per WG with one WG per CU
-    if (tpw > fill) tpw = fill;
-    return tpw;
-}
+// Launch shape of the streaming kernel.  Eight waves per workgroup (two per
+// SIMD: one wave alone leaves the decode's dependent-issue gaps unfilled) and
+// about one workgroup per CU, each owning a run of 16-row tiles.
+struct GemvPlan {
+    int waves, tpw;
+    bool deep;  // prefetch depth gemv_depth(r), else GEMV_DEPTH_SHORT
+};
 
-constexpr int64_t GEMV_SINGLE_TARGET = 256 << 10;
-constexpr int64_t GEMV_GROUP_TARGET = 256 << 10;
+static GemvPlan gemv_plan(int n, int k, int r, int cu_count) {
+    const int tiles = (n + 15) / 16;
+    GemvPlan p;
+    p.waves = GEMV_MAX_WAVES;
+    int tpw = (tiles + cu_count / 2) / cu_count;  // about one workgroup per CU
+    if (tpw > GEMV_MAX_TILES) tpw = GEMV_MAX_TILES;
+    if (tpw < 1) tpw = 1;
+    p.tpw = tpw;
+    const int nsets = (k / 128 + 3) / 4;
+    const int steps = (nsets + p.waves - 1) / p.waves * tpw;  // per wave, at most
+    p.deep = gemv_depth(r) > GEMV_DEPTH_SHORT && steps >= 4;
+    return p;
+}
 
 static bool gemv_streamable(int k);
 
@@ -355,15 +384,21 @@ static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int tiles = (a.n + 15) / 16;
     for (int64_t b = 0; b < a.batch; ++b) {  // one batch row per launch
         if (!gemv_streamable(a.k)) {
-            hipLaunchKernelGGL(gemv_odd_kernel<R>, dim3(tiles), dim3(64 * GEMV_WAVES), 0, stream,
+            hipLaunchKernelGGL(gemv_odd_kernel<R>, dim3(tiles), dim3(64 * GEMV_ODD_WAVES), 0, stream,
                                a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k,
                                a.y + b * a.n);
         } else {
-            const int tpw = gemv_tpw(a.n, a.k, R, cu_count, GEMV_SINGLE_TARGET);
-            hipLaunchKernelGGL(gemv_kernel<R>, dim3((tiles + tpw - 1) / tpw),
-                               dim3(64 * GEMV_WAVES), gemv_lds_bytes(a.k, GEMV_WAVES), stream,
-                               a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k, tiles,
-                               tpw, a.y + b * a.n);
+            const GemvPlan p = gemv_plan(a.n, a.k, R, cu_count);
+            const dim3 grid((tiles + p.tpw - 1) / p.tpw), block(64 * p.waves);
+            const size_t lds = gemv_lds_bytes(p.waves, p.tpw);
+            if (p.deep)
+                hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R)>), grid, block, lds, stream,
+                                   a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k, tiles,
+                                   p.tpw, a.y + b * a.n);
+            else
+                hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT>), grid, block, lds, stream,
+                                   a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k, tiles,
+                                   p.tpw, a.y + b * a.n);
         }
     }
 }
@@ -384,20 +419,19 @@ hipError_t launch_gemv(int r, const QgemmArgs &a, int cu_count, hipStream_t stre
 }
 
 void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
-    (void)cu_count;
-    if (!gemv_streamable(a.k))
+    if (!gemv_streamable(a.k)) {
         snprintf(out, len, "nbw::gemv_odd_kernel<%d>", r);
-    else
-        snprintf(out, len, "nbw::gemv_kernel<%d>", r);
+    } else {
+        const GemvPlan p = gemv_plan(a.n, a.k, r, cu_count);
+        snprintf(out, len, "nbw::gemv_kernel<%d, %d>", r, p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT);
+    }
 }
 
 int gemv_group_capacity() { return GEMV_MAX_GROUP; }
 
-// The streaming kernel stages X in LDS and reads scales as aligned words:
-// it takes even group counts whose X fits in 64 KB of LDS.
-static bool gemv_streamable(int k) {
-    return ((k / 128) & 1) == 0 && gemv_lds_bytes(k, GEMV_WAVES) <= 64 * 1024;
-}
+// The streaming kernel reads scales as aligned 32-bit words: it takes even
+// group counts (every other shape goes to the plain one-tile kernel).
+static bool gemv_streamable(int k) { return ((k / 128) & 1) == 0; }
 
 bool gemv_group_eligible(const QgemmArgs &a) { return a.batch == 1 && gemv_streamable(a.k); }
 
@@ -405,7 +439,7 @@ hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, i
                              hipStream_t stream) {
     GemvGroup grp = {};
     grp.count = count;
-    int items = 0, kmax = 128;
+    int items = 0, slots = 1;
     for (int j = 0; j < count; ++j) {
         const QgemmArgs &a = probs[j];
         GemvJob &J = grp.job[j];
@@ -418,13 +452,14 @@ hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, i
         J.k = a.k;
         J.r = rs[j];
         J.tiles = (a.n + 15) / 16;
-        J.tpw = gemv_tpw(a.n, a.k, rs[j], cu_count, GEMV_GROUP_TARGET);
+        J.tpw = gemv_plan(a.n, a.k, rs[j], cu_count).tpw;
+        if (J.tpw > slots) slots = J.tpw;
         J.item_begin = items;
         items += (J.tiles + J.tpw - 1) / J.tpw;
-        if (a.k > kmax) kmax = a.k;
     }
-    hipLaunchKernelGGL(gemv_group_kernel, dim3(items), dim3(64 * GEMV_WAVES),
-                       gemv_lds_bytes(kmax, GEMV_WAVES), stream, grp);
+    grp.slots = slots;
+    hipLaunchKernelGGL(gemv_group_kernel, dim3(items), dim3(64 * GEMV_MAX_WAVES),
+                       gemv_lds_bytes(GEMV_MAX_WAVES, slots), stream, grp);
     return hipGetLastError();
 }
 
