@@ -1,0 +1,281 @@
+// gemm.hip -- large-batch dequant-GEMM on the matrix cores, gfx950.
+//
+// Y[b][i] = sum_j X[b][j] * s[i][j/128] * 2^(8-r) * (q_r[i][j] + 1/2 - 2^(r-1)),
+// the r-bit child of a sliceable parent (MatGPTQ: Efficient and Accurate
+// Inference over Nested Quantized Models, Abstract: kernels that support
+// batch sizes beyond one; Figure 1: batch sweep against a dense matmul).  At
+// large batch the product is a real dense contraction, bound by the MFMA
+// rate, so the weights are decoded once per workgroup tile and feed
+// v_mfma_f32_32x32x16_bf16 directly.
+//
+// Layout of the work (D = A.B with A = X rows, B = decoded weights):
+//  - a workgroup owns 128 batch rows x 256 weight rows and a range of 128-wide
+//    groups along k; its 8 waves (two per SIMD) each own one block of 32
+//    weight rows and all 128 batch rows (four 32-row blocks): 4 accumulator
+//    tiles of 32 x 32.
+//  - B operands never touch LDS: lane (row l%32, half h = l/32) of a weight
+//    block loads 8 bytes of each plane -- words 2h and 2h+1 of its row's
+//    16-byte chunk -- and decodes them (decode.h) into the 32 bf16 pairs of
+//    columns 64h .. 64h+63 of the group; MFMA j takes pairs 4j..4j+3, i.e.
+//    columns 64h + 8j .. 64h + 8j + 7, in natural order.
+//  - A operands come from an LDS copy of the group's X tile (double
+//    buffered, rows padded against bank conflicts): lane (row l%32, half h)
+//    reads the same 8 columns 64h + 8j .. +7, so the k order of both
+//    operands agrees.
+//  - every 8-MFMA chain covers one group and starts from the group's
+//    correction (sum_k x_k * (1/2 - 2^(r-1) - offset_k), X only); the group
+//    scale, one per lane (lane = weight row), is folded in fp32 right after.
+//    Two batch blocks run their chains interleaved, so no MFMA waits on the
+//    one before it.
+//  - X is loaded one group ahead (thread (row, quarter) moves 32 columns
+//    and forms their share of the row's correction), planes and scales two
+//    groups ahead; one barrier per group hands the X buffers over.
+#include <cstdio>
+
+#include "decode.h"
+#include "launch.h"
+
+namespace nbw {
+
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int GEMM_BM = 128;        // batch rows per workgroup
+constexpr int GEMM_WAVES = 8;       // waves per workgroup, one 32-row weight block each
+constexpr int GEMM_BN = 32 * GEMM_WAVES;  // weight rows per workgroup
+constexpr int GEMM_XSTRIDE = 136;   // bf16 per LDS row of the X tile (128 + 8 padding)
+
+__device__ __forceinline__ float gm_dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ f32x16_t gm_mfma(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// grid: (ceil(n / 256), ceil(batch / 128), splits); block 512.  Groups
+// [z * gps, min(G, (z + 1) * gps)) of k.  With atomic != 0 the result is added
+// to y (which the launcher has cleared); otherwise it is stored.
+template <int R>
+__global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
+    const uint16_t *__restrict__ x, int batch, const uint8_t *__restrict__ planes,
+    int64_t plane_bytes, const uint16_t *__restrict__ scales, int n, int k, int gps,
+    float *__restrict__ y, int atomic) {
+    __shared__ __align__(16) uint16_t xs[2][GEMM_BM * GEMM_XSTRIDE];
+    __shared__ __align__(16) float corr[2][GEMM_BM];
+    constexpr int NPH = Phases<R>::count;
+
+    const int G = k >> 7;
+    const int g_begin = blockIdx.z * gps;
+    const int g_end = min(G, g_begin + gps);
+    if (g_begin >= g_end) return;  // uniform over the workgroup
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int b0 = blockIdx.y * GEMM_BM;
+    const int npad = (n + 15) & ~15;
+
+    // This lane's weight row and the base of its 8 bytes in plane 0, group 0.
+    const int nrow = blockIdx.x * GEMM_BN + 32 * w + l32;
+    const int rc = min(nrow, npad - 1);
+    const uint8_t *pbase = planes + ((int64_t)(rc >> 4) * G * 16 + (rc & 15)) * 16 + 8 * h;
+    const uint16_t *sbase = scales + (int64_t)min(nrow, n - 1) * G;
+
+    // X staging: thread (xr, qq) moves columns 32qq .. 32qq+31 (word qq of the
+    // group: bf16 pairs m = 0..15) of batch row b0 + xr.
+    const int xr = tid >> 2, qq = tid & 3;
+    const uint16_t *xrow = x + (int64_t)min(b0 + xr, batch - 1) * k + 32 * qq;
+    u32x4_t xv[4];
+    auto load_x = [&](int g) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            xv[c] = *reinterpret_cast<const u32x4_t *>(xrow + 128 * g + 8 * c);
+    };
+    auto stage_x = [&](int buf) {
+        const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            *reinterpret_cast<u32x4_t *>(&xs[buf][xr * GEMM_XSTRIDE + 32 * qq + 8 * c]) = xv[c];
+            part = fmaf(pair_coef<R>(4 * c + 0), gm_dot2(one, xv[c].x, 0.f), part);
+            part = fmaf(pair_coef<R>(4 * c + 1), gm_dot2(one, xv[c].y, 0.f), part);
+            part = fmaf(pair_coef<R>(4 * c + 2), gm_dot2(one, xv[c].z, 0.f), part);
+            part = fmaf(pair_coef<R>(4 * c + 3), gm_dot2(one, xv[c].w, 0.f), part);
+        }
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        if (qq == 0) corr[buf][xr] = part;
+    };
+
+    // Planes and scale of groups g (cur) and g + 1 (next).
+    u32x2_t pw[2][R];
+    uint32_t sraw[2];
+    auto load_w = [&](int slot, int g) {
+        const uint8_t *c = pbase + (int64_t)g * 256;
+#pragma unroll
+        for (int p = 0; p < R; ++p)
+            pw[slot][p] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2_t *>(c + (int64_t)p * plane_bytes));
+        sraw[slot] = sbase[g];
+    };
+
+    load_x(g_begin);
+    load_w(0, g_begin);
+    if (g_begin + 1 < g_end) load_w(1, g_begin + 1);
+    stage_x(0);
+    __syncthreads();
+
+    f32x16_t acc[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[bb][v] = 0.f;
+
+    for (int g = g_begin; g < g_end; ++g) {
+        const int buf = (g - g_begin) & 1;
+
+        // Decode this group's weight operands: Bop[ph][pair].
+        uint32_t Bop[NPH][32];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint32_t P[R];
+#pragma unroll
+            for (int p = 0; p < R; ++p) P[p] = q ? pw[0][p].y : pw[0][p].x;
+            uint32_t D0[16], D1[16];
+            decode_word<R>(P, D0, D1);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                Bop[0][16 * q + m] = D0[m];
+                if constexpr (NPH == 2) Bop[NPH - 1][16 * q + m] = D1[m];
+            }
+        }
+        const float s = nrow < n ? __uint_as_float(sraw[0] << 16) : 0.f;
+
+        // Shift the plane window and fetch two groups ahead; X one ahead.
+#pragma unroll
+        for (int p = 0; p < R; ++p) pw[0][p] = pw[1][p];
+        sraw[0] = sraw[1];
+        if (g + 2 < g_end) load_w(1, g + 2);
+        const bool more = g + 1 < g_end;
+        if (more) load_x(g + 1);
+
+#pragma unroll
+        for (int bp = 0; bp < 2; ++bp) {
+            // Two batch blocks, chains interleaved; each starts from the
+            // correction of its batch rows.
+            f32x16_t Pc[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int bb = 2 * bp + e;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 c4 =
+                        *reinterpret_cast<const float4 *>(&corr[buf][32 * bb + 8 * q + 4 * h]);
+                    Pc[e][4 * q] = c4.x; Pc[e][4 * q + 1] = c4.y;
+                    Pc[e][4 * q + 2] = c4.z; Pc[e][4 * q + 3] = c4.w;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int bb = 2 * bp + e;
+                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
+                        &xs[buf][(32 * bb + l32) * GEMM_XSTRIDE + 64 * h + 8 * j]);
+#pragma unroll
+                    for (int ph = 0; ph < NPH; ++ph) {
+                        const u32x4_t wv = {Bop[ph][4 * j], Bop[ph][4 * j + 1], Bop[ph][4 * j + 2],
+                                            Bop[ph][4 * j + 3]};
+                        Pc[e] = gm_mfma(a, wv, Pc[e]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[2 * bp + e][v] = fmaf(s, Pc[e][v], acc[2 * bp + e][v]);
+        }
+
+        if (more) stage_x(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane holds rows b0 + 32bb + 8(v/4) + 4h + v%4 of column nrow.
+    if (nrow < n) {
+        const float post = (float)(1 << (8 - R));
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int b = b0 + 32 * bb + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (b >= batch) continue;
+                float *dst = y + (int64_t)b * n + nrow;
+                const float val = acc[bb][v] * post;
+                if (atomic)
+                    __hip_atomic_fetch_add(dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    *dst = val;
+            }
+    }
+}
+
+// Clears y before a split-k launch adds its partial sums.
+__global__ void gemm_zero_kernel(float *__restrict__ y, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = i; e < count; e += stride) y[e] = 0.f;
+}
+
+// Split k only when the output tiles leave most CUs idle; each split keeps
+// at least 4 groups.
+static int gemm_splits(const QgemmArgs &a, int cu_count) {
+    const int tiles = (a.n + GEMM_BN - 1) / GEMM_BN * (int)((a.batch + GEMM_BM - 1) / GEMM_BM);
+    const int G = a.k / 128;
+    int s = 1;
+    while (tiles * s * 2 <= cu_count && G / (2 * s) >= 4) s *= 2;
+    return s;
+}
+
+template <int R>
+static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
+    const int G = a.k / 128;
+    const int splits = gemm_splits(a, cu_count);
+    const int gps = (G + splits - 1) / splits;
+    if (splits > 1) {
+        const int64_t count = a.batch * (int64_t)a.n;
+        const int64_t blocks = (count + 255) / 256;
+        hipLaunchKernelGGL(gemm_zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                           dim3(256), 0, stream, a.y, count);
+    }
+    const dim3 grid((a.n + GEMM_BN - 1) / GEMM_BN, (unsigned)((a.batch + GEMM_BM - 1) / GEMM_BM),
+                    splits);
+    hipLaunchKernelGGL(gemm_kernel<R>, grid, dim3(64 * GEMM_WAVES), 0, stream, a.x, (int)a.batch, a.planes,
+                       a.plane_bytes, a.scales, a.n, a.k, gps, a.y, splits > 1 ? 1 : 0);
+}
+
+hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {
+    switch (r) {
+    case 1: launch_r<1>(a, cu_count, stream); break;
+    case 2: launch_r<2>(a, cu_count, stream); break;
+    case 3: launch_r<3>(a, cu_count, stream); break;
+    case 4: launch_r<4>(a, cu_count, stream); break;
+    case 5: launch_r<5>(a, cu_count, stream); break;
+    case 6: launch_r<6>(a, cu_count, stream); break;
+    case 7: launch_r<7>(a, cu_count, stream); break;
+    case 8: launch_r<8>(a, cu_count, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+void gemm_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
+    (void)a;
+    (void)cu_count;
+    snprintf(out, len, "nbw::gemm_kernel<%d>", r);
+}
+
+}  // namespace nbw

@@ -190,14 +190,4 @@ hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t st
     return hipGetLastError();
 }
 
-// Large batches reuse the small-batch kernel over 16-row batch slices until
-// the dedicated large-batch kernel lands.
-hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {
-    return launch_smallb(r, a, cu_count, stream);
-}
-
-void gemm_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
-    smallb_name(r, a, cu_count, out, len);
-}
-
 }  // namespace nbw
