@@ -56,6 +56,12 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip batch 4/16/256 and pack timing")
     ap.add_argument("--copies", type=int, default=0, help="parent copies in the rotation (0 = auto)")
     ap.add_argument("--b1-kernel", default="auto", help="kernel for the batch-1 step (auto, gemv, smallb)")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run only a plain device copy of known size and the dominant batch-1 "
+                         "kernel's launches (for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="derive per-launch HBM traffic from two rocprofv3 --pmc output folders "
+                         "of --pmc-probe and write it under profiles/")
     return ap.parse_args()
 
 
@@ -189,8 +195,122 @@ def dominant(durs, batch):
     return name, t
 
 
+# ---------------------------------------------------------------- HBM traffic
+#
+# rocprofv3's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the
+# same counters read for a plain device copy of known size.  The probe launches
+# the dominant batch-1 kernel on the shapes it runs in the step (r = 4:
+# gate_up and down), each from its own parent copy.
+
+PROBE_COPY_BYTES = 512 << 20
+PROBE_SHAPES = ("gate_up", "down")
+PROBE_R = 4
+PROBE_LAUNCHES = 6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_r4_b1.txt")
+KERNEL_SOURCES = ("nested_bit_weight_amd/csrc/gemv.hip", "nested_bit_weight_amd/csrc/decode.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_probe(torch, nbw, synth):
+    src = torch.empty(PROBE_COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)  # the reference dispatch: PROBE_COPY_BYTES read + written
+    torch.cuda.synchronize()
+    del src, dst
+    layer = Layer(torch, nbw, synth, "llama3.1-8b", PROBE_LAUNCHES)
+    for L in layer.lin:
+        if L["name"] not in PROBE_SHAPES:
+            continue
+        y = torch.empty((1, L["n"]), dtype=torch.float32, device="cuda")
+        for c in range(layer.copies):
+            nbw.qgemm(L["x1"], L["w"][c].slice_view(PROBE_R), L["s"][c], PROBE_R, out=y)
+            torch.cuda.synchronize()
+    log(f"pmc probe: copy {PROBE_COPY_BYTES} B; kernel {nbw.kernel_name(1, 28672, 4096, PROBE_R)} "
+        f"x {PROBE_LAUNCHES} on {PROBE_SHAPES}")
+
+
+def _pmc_rows(folder, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    out = []
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    out.append((int(row["Dispatch_Id"]), row["Kernel_Name"], float(row["Counter_Value"])))
+    return sorted(out)
+
+
+def traffic_from(fetch_dir, write_dir):
+    import synth
+    res = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(folder, counter)
+        copy = [v for _, name, v in rows if "copybuffer" in name.lower()]
+        kern = [v for _, name, v in rows if "gemv_kernel<4" in name]
+        if not copy or not kern:
+            raise SystemExit(f"{counter}: probe dispatches not found in {folder}")
+        factor = PROBE_COPY_BYTES / (max(copy) * 1024.0)
+        res[counter] = {"copy_kib": max(copy), "factor": factor,
+                        "kernel_kib_avg": sum(kern) / len(kern), "launches": len(kern),
+                        "kernel_bytes_avg": sum(kern) / len(kern) * 1024.0 * factor}
+    shapes = {nm: (n, k) for nm, n, k in synth.WORKLOADS["llama3.1-8b"]}
+    alg = sum(PROBE_R * shapes[s][0] * shapes[s][1] // 8 for s in PROBE_SHAPES) / len(PROBE_SHAPES)
+    traffic = res["FETCH_SIZE"]["kernel_bytes_avg"] + res["WRITE_SIZE"]["kernel_bytes_avg"]
+    lines = [
+        "# HBM traffic of the dominant batch-1 kernel (gemv_kernel<4, *>, Llama-3.1-8B gate_up and down, r = 4)",
+        "",
+        "Commands (repository root, one MI355X; one counter per pass):",
+        "  rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-probe",
+        "  rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -- python3 bench.py --pmc-probe",
+        "  python3 bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "",
+        f"reference copy: {PROBE_COPY_BYTES} bytes read and written by one device copy dispatch",
+    ]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[c]
+        lines.append(f"{c}: copy counts {r['copy_kib']:.1f} KiB -> factor {r['factor']:.4f} bytes per reported byte; "
+                     f"kernel {r['kernel_kib_avg']:.1f} KiB avg over {r['launches']} launches -> "
+                     f"{r['kernel_bytes_avg']:.0f} bytes")
+    lines += [f"algorithmic plane bytes per launch (avg of the two shapes): {alg:.0f}",
+              f"traffic_bytes_per_launch: {traffic:.0f}",
+              f"traffic_over_algorithmic: {traffic / alg:.4f}",
+              f"kernel_source_sha256_16: {kernel_source_hash()}"]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stored_traffic():
+    """Per-launch HBM bytes from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines() if ": " in line)
+        if kv.get("kernel_source_sha256_16", "").strip() != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -208,6 +328,10 @@ def main():
     torch.cuda.set_device(0)
     nbw.library()  # fails loudly if the HIP library is not built
     log(f"libnbw {nbw.version()} on {torch.cuda.get_device_name(0)}")
+
+    if args.pmc_probe:
+        pmc_probe(torch, nbw, synth)
+        return
 
     t = time.time()
     layer = Layer(torch, nbw, synth, "llama3.1-8b", args.copies)
@@ -231,8 +355,10 @@ def main():
     dom_name, dom = dominant(durs, 1)
     dom_avg_us = dom["us"] / dom["launches"]
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    traffic = stored_traffic() if dom_name.startswith("nbw::gemv_kernel<4") else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": round(traffic) if traffic else None,
                 "kernel": dom_name, "avg_launch_us": round(dom_avg_us, 2),
                 "bytes_per_launch": dom["bytes"] // dom["launches"],
                 "launches_per_step": dom["launches"]}
