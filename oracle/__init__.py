@@ -54,6 +54,12 @@ def _configure(lib):
     lib.nbwo_qgemm_rows.restype = i32
     lib.nbwo_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.nbwo_bf16_to_double.restype = dp
+    lib.nbwo_dequant_value_asym.argtypes = [dp, dp, i32, i32]
+    lib.nbwo_dequant_value_asym.restype = dp
+    lib.nbwo_qgemm_asym_rows.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, vp, i64, vp]
+    lib.nbwo_qgemm_asym_rows.restype = i32
+    lib.nbwo_choose_codes.argtypes = [vp, i64, i64, vp, vp, vp, i32, vp]
+    lib.nbwo_choose_codes.restype = None
     return lib
 
 
@@ -166,3 +172,47 @@ def bf16_to_f64(h: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns (uint16) to float64."""
     h = np.asarray(h, dtype=np.uint16)
     return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dequant_value_asym(s: float, z: float, q: int, r: int) -> float:
+    """Asymmetric child value s * (2^(8-r) * (q + 1/2) - 1/2 - z)."""
+    return float(_load().nbwo_dequant_value_asym(float(s), float(z), int(q), int(r)))
+
+
+def qgemm_asym(x_bf16: np.ndarray, planes: np.ndarray, scales_bf16: np.ndarray,
+               zeros_bf16: np.ndarray, n: int, k: int, r: int, rows=None) -> np.ndarray:
+    """fp64 Y [batch][len(rows)] of the asymmetric child (all rows by default)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    if x.ndim != 2 or x.shape[1] != k or x.shape[0] < 1:
+        raise ValueError(f"x must be [batch][{k}], got {x.shape}")
+    planes = _check_planes(planes, n, k, r)
+    scales = _check_scales(scales_bf16, n, k)
+    zeros = _check_scales(zeros_bf16, n, k)
+    rows = np.arange(n, dtype=np.int64) if rows is None else \
+        np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    if rows.size and (rows.min() < 0 or rows.max() >= n):
+        raise ValueError("row index out of range")
+    out = np.empty((x.shape[0], rows.size), dtype=np.float64)
+    rc = _load().nbwo_qgemm_asym_rows(_ptr(x), x.shape[0], _ptr(planes), _ptr(scales),
+                                      _ptr(zeros), n, k, r, _ptr(rows), rows.size, _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle qgemm_asym: allocation failed")
+    return out
+
+
+def choose_codes(w_f32: np.ndarray, scales_bf16: np.ndarray, widths, lambdas) -> np.ndarray:
+    """Parent codes uint8 [n][k] minimising the lambda-weighted child errors (brute force)."""
+    w = np.ascontiguousarray(w_f32, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be [n][k]")
+    n, k = w.shape
+    _check_shape(n, k)
+    scales = _check_scales(scales_bf16, n, k)
+    widths = np.ascontiguousarray(widths, dtype=np.int32).reshape(-1)
+    lambdas = np.ascontiguousarray(lambdas, dtype=np.float64).reshape(-1)
+    if widths.size != lambdas.size or widths.size < 1 or widths.min() < 1 or widths.max() > 8:
+        raise ValueError("widths (1..8) and lambdas must be non-empty and of equal length")
+    out = np.empty((n, k), dtype=np.uint8)
+    _load().nbwo_choose_codes(_ptr(w), n, k, _ptr(scales), _ptr(widths), _ptr(lambdas),
+                              int(widths.size), _ptr(out))
+    return out

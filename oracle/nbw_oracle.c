@@ -192,3 +192,100 @@ int nbwo_qgemm_rows(const uint16_t *x, int64_t batch, const uint8_t *planes,
     }
     return fail ? -1 : 0;
 }
+
+/* ---- asymmetric children ------------------------------------------------ */
+/*
+ * The pages evaluate an asymmetric variant (MatGPTQ: Efficient and Accurate
+ * Inference over Nested Quantized Models, Tables 4-7, "asymmetric MatGPTQ")
+ * without stating its formula.  Reading used here: the parent grid is
+ * s * (c - z) with a per-(row, group) zero point z, and an r-bit child takes
+ * the mean of its 2^(8-r) parent values, exactly as the symmetric grid does:
+ *     w = s * (2^(8-r) * (q_r + 1/2) - 1/2 - z).
+ * With z = 127.5 this is the symmetric closed form above.
+ */
+double nbwo_dequant_value_asym(double s, double z, int q, int r) {
+    return s * (ldexp(1.0, 8 - r) * ((double)q + 0.5) - 0.5 - z);
+}
+
+static void qgemm_row_asym(const uint16_t *x, int64_t batch, const uint8_t *planes,
+                           const uint16_t *scales, const uint16_t *zeros, int64_t n, int64_t k,
+                           int r, int64_t i, double *wrow, double *out, int64_t stride) {
+    int64_t groups = k / 128;
+    for (int64_t j = 0; j < k; ++j) {
+        int q = 0;
+        for (int p = 0; p < r; ++p)
+            q = 2 * q + read_bit(planes, n, k, p, i, j);
+        double s = nbwo_bf16_to_double(scales[i * groups + j / 128]);
+        double z = nbwo_bf16_to_double(zeros[i * groups + j / 128]);
+        wrow[j] = nbwo_dequant_value_asym(s, z, q, r);
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < k; ++j)
+            acc += wrow[j] * nbwo_bf16_to_double(x[b * k + j]);
+        out[b * stride] = acc;
+    }
+}
+
+/* Asymmetric product for selected output rows (all rows: rows = 0..n-1);
+ * zeros bf16 [n][k/128] like the scales.  y is [batch][nrows]. */
+int nbwo_qgemm_asym_rows(const uint16_t *x, int64_t batch, const uint8_t *planes,
+                         const uint16_t *scales, const uint16_t *zeros, int64_t n, int64_t k,
+                         int r, const int64_t *rows, int64_t nrows, double *y) {
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < nrows; ++t) {
+        double *wrow = (double *)malloc((size_t)k * sizeof(double));
+        if (!wrow) {
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        qgemm_row_asym(x, batch, planes, scales, zeros, n, k, r, rows[t], wrow, y + t, nrows);
+        free(wrow);
+    }
+    return fail ? -1 : 0;
+}
+
+/* ---- data-free multi-precision code choice ----------------------------- */
+/*
+ * For each weight w (fp32) with its group scale s, choose the parent code
+ * c in [0, 255] that minimises the weighted squared error of the children it
+ * serves (MatGPTQ: Accurate and Efficient Post-Training Matryoshka
+ * Quantization, abstract: one parent serves several precisions; MatGPTQ:
+ * Efficient and Accurate Inference over Nested Quantized Models, Section 3
+ * on the per-precision weights lambda_3, lambda_4, lambda_8):
+ *     loss(c) = sum_t lambda_t * (w - dequant(s, c >> (8 - r_t), r_t))^2,
+ * for the widths r_t in `widths` (nw of them).  Every code is tried in order
+ * 0..255; the first code with the smallest loss wins.  All arithmetic is
+ * IEEE double, one operation at a time, in this order: e = w - d; e2 = e * e;
+ * term = lambda * e2; loss accumulated left to right over `widths`.
+ */
+void nbwo_choose_codes(const float *w, int64_t n, int64_t k, const uint16_t *scales,
+                       const int *widths, const double *lambdas, int nw, uint8_t *codes) {
+    int64_t groups = k / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < k; ++j) {
+            double wv = (double)w[i * k + j];
+            double s = nbwo_bf16_to_double(scales[i * groups + j / 128]);
+            int best = 0;
+            double best_loss = 0.0;
+            for (int c = 0; c < 256; ++c) {
+                double loss = 0.0;
+                for (int t = 0; t < nw; ++t) {
+                    int r = widths[t];
+                    double d = nbwo_dequant_value(s, c >> (8 - r), r);
+                    double e = wv - d;
+                    double e2 = e * e;
+                    double term = lambdas[t] * e2;
+                    loss = loss + term;
+                }
+                if (c == 0 || loss < best_loss) {
+                    best = c;
+                    best_loss = loss;
+                }
+            }
+            codes[i * k + j] = (uint8_t)best;
+        }
+}

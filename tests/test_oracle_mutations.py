@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_pins_ext as pins_ext
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "nbw_oracle.c")
@@ -25,10 +26,23 @@ MUTANTS = {
     "wrong_exponent": ("s * ldexp(1.0, 8 - r)", "s * ldexp(1.0, 7 - r)"),
     "shifted_scale_group": ("double s = nbwo_bf16_to_double(scales[i * groups + j / 128]);\n        wrow",
                             "double s = nbwo_bf16_to_double(scales[i * groups + (j / 128 + 1) % groups]);\n        wrow"),
-    "transposed_x": ("nbwo_bf16_to_double(x[b * k + j])", "nbwo_bf16_to_double(x[j * batch + b])"),
+    "transposed_x": ("acc += nbwo_bf16_to_double(x[b * k + j]) * wrow[j];",
+                     "acc += nbwo_bf16_to_double(x[j * batch + b]) * wrow[j];"),
+    "asym_transposed_x": ("acc += wrow[j] * nbwo_bf16_to_double(x[b * k + j]);",
+                          "acc += wrow[j] * nbwo_bf16_to_double(x[j * batch + b]);"),
     "wrong_sign": ("acc += nbwo_bf16_to_double", "acc -= nbwo_bf16_to_double"),
     "lsb_first_unpack": ("v = 2 * v + read_bit(planes, n, k, p, i, j);",
                          "v = v + (read_bit(planes, n, k, p, i, j) << p);"),
+    # asymmetric children
+    "asym_dropped_half": ("((double)q + 0.5) - 0.5 - z)", "((double)q + 0.5) - z)"),
+    "asym_zero_sign": ("((double)q + 0.5) - 0.5 - z)", "((double)q + 0.5) - 0.5 + z)"),
+    "asym_zero_of_next_group": ("zeros[i * groups + j / 128]",
+                                "zeros[i * groups + (j / 128 + 1) % groups]"),
+    # code chooser
+    "choose_last_of_ties": ("if (c == 0 || loss < best_loss)", "if (c == 0 || loss <= best_loss)"),
+    "choose_wrong_child_shift": ("nbwo_dequant_value(s, c >> (8 - r), r)",
+                                 "nbwo_dequant_value(s, c >> (7 - r), r)"),
+    "choose_ignores_lambda": ("double term = lambdas[t] * e2;", "double term = e2;"),
 }
 
 
@@ -42,6 +56,16 @@ def _pin_calls():
              lambda: pins.test_qgemm_identity_activations_give_weights(4)]
     for row in pins._golden_layout():
         calls.append(lambda row=row: pins.test_layout_worked_examples(*row))
+    calls += [lambda: pins_ext.test_asym_with_midpoint_zero_is_symmetric(3),
+              pins_ext.test_asym_r8_is_parent_grid,
+              lambda: pins_ext.test_asym_child_is_mean_of_parent_bucket(2),
+              lambda: pins_ext.test_asym_qgemm_exact_rational_bruteforce(3),
+              pins_ext.test_asym_qgemm_reduces_to_symmetric_and_is_linear_in_z,
+              pins_ext.test_choose_single_width8_is_nearest_grid_point,
+              pins_ext.test_choose_single_width4_takes_first_code_of_nearest_level,
+              pins_ext.test_choose_exact_rational_bruteforce,
+              pins_ext.test_choose_zero_weight_widths_drop_out,
+              pins_ext.test_choose_all_zero_lambdas_tie_to_code_zero]
     return calls
 
 
