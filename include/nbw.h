@@ -131,6 +131,54 @@ nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *
                             const void *scales_bf16, int32_t r, float *y, nbw_kernel kernel,
                             void *stream);
 
+/* Output element type of nbw_qgemm_ex. */
+typedef enum nbw_ydtype {
+    NBW_Y_F32 = 0,  /* fp32 (the accumulation itself) */
+    NBW_Y_BF16 = 1  /* bf16, the fp32 result rounded to nearest even */
+} nbw_ydtype;
+
+/* Options of nbw_qgemm_ex.  A zero-filled struct gives nbw_qgemm's
+ * behaviour (dense X and Y, fp32 Y, symmetric children, automatic kernel). */
+typedef struct nbw_qgemm_opts {
+    int64_t ldx;        /* elements from one X row to the next: 0 (= k) or >= k,
+                           a multiple of 8 (X rows stay 16-byte aligned) */
+    int64_t ldy;        /* elements from one Y row to the next: 0 (= n) or >= n */
+    int32_t y_dtype;    /* nbw_ydtype */
+    int32_t kernel;     /* nbw_kernel */
+    const void *zeros_bf16; /* NULL: symmetric children.  Otherwise asymmetric
+                           children, bf16 zero points [n][k/128] (4-byte
+                           aligned, the scales' layout): the parent grid is
+                           s * (c - z) and an r-bit child is the mean of its
+                           parent bucket, w = s * (2^(8-r) * (q_r + 1/2) - 1/2 - z)
+                           (the pages evaluate an asymmetric variant, MatGPTQ v2
+                           Tables 4-7, without stating its formula; z = 127.5
+                           gives the symmetric child exactly). */
+} nbw_qgemm_opts;
+
+/* nbw_qgemm with row strides, a bf16 output and asymmetric children
+ * (opts == NULL: as nbw_qgemm).  y points at fp32 or bf16 elements per
+ * opts->y_dtype; only the first n elements of each Y row are written.  Same
+ * errors as nbw_qgemm, plus NBW_EINVAL for a stride below k or n and
+ * NBW_EALIGN for a stride that breaks the row alignment; NBW_EUNSUPPORTED
+ * for an unknown y_dtype or kernel. */
+nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                        const void *scales_bf16, int32_t r, void *y, const nbw_qgemm_opts *opts,
+                        void *stream);
+
+/* Data-free parent-code choice: for every fp32 weight w[i][j] (device, [n][k])
+ * with group scale s[i][j/128] (device bf16 [n][k/128]), the code c in 0..255
+ * minimising sum_t lambdas[t] * (w - dequant_{widths[t]}(c))^2 over the
+ * children r = widths[t] (symmetric closed form above); the first code with
+ * the smallest loss wins (MatGPTQ v2, Section 3: per-precision weights
+ * lambda_r; MatGPTQ v1 abstract: one parent serves every sliced width).  Every
+ * code is tried in IEEE double, one rounded operation at a time.  widths and
+ * lambdas are HOST arrays of nw (1..8) entries; widths in 1..8, lambdas >= 0
+ * and finite.  codes_out: device uint8 [n][k] (ready for nbw_pack_bitplanes).
+ * Runs on `stream`. */
+nbw_status nbw_choose_codes(const float *w, int64_t n, int64_t k, const void *scales_bf16,
+                            const int32_t *widths, const double *lambdas, int32_t nw,
+                            uint8_t *codes_out, void *stream);
+
 /* One product of a grouped call: Y = X . dequant_r(W)^T for the r-bit child
  * of `w`, with the same arguments as nbw_qgemm. */
 typedef struct nbw_problem {

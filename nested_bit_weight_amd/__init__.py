@@ -44,6 +44,14 @@ class WView(ctypes.Structure):
                 ("plane_bytes", ctypes.c_int64)]
 
 
+class QgemmOpts(ctypes.Structure):
+    _fields_ = [("ldx", ctypes.c_int64), ("ldy", ctypes.c_int64), ("y_dtype", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("zeros_bf16", ctypes.c_void_p)]
+
+
+Y_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
 class Problem(ctypes.Structure):
     _fields_ = [("x_bf16", ctypes.c_void_p), ("batch", ctypes.c_int64), ("w", WView),
                 ("scales_bf16", ctypes.c_void_p), ("r", ctypes.c_int32), ("y", ctypes.c_void_p)]
@@ -52,8 +60,8 @@ class Problem(ctypes.Structure):
 _LIB = None
 
 EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
-           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_grouped",
-           "nbw_unpack_codes",
+           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex", "nbw_qgemm_grouped",
+           "nbw_choose_codes", "nbw_unpack_codes",
            "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
 
 
@@ -79,6 +87,11 @@ def _lib():
         lib.nbw_qgemm.restype = ctypes.c_int
         lib.nbw_qgemm_kernel.argtypes = [vp, i64, pv, vp, i32, vp, ctypes.c_int, vp]
         lib.nbw_qgemm_kernel.restype = ctypes.c_int
+        lib.nbw_qgemm_ex.argtypes = [vp, i64, pv, vp, i32, vp, ctypes.POINTER(QgemmOpts), vp]
+        lib.nbw_qgemm_ex.restype = ctypes.c_int
+        lib.nbw_choose_codes.argtypes = [vp, i64, i64, vp, ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_double), i32, vp, vp]
+        lib.nbw_choose_codes.restype = ctypes.c_int
         lib.nbw_qgemm_grouped.argtypes = [ctypes.POINTER(Problem), i32, vp]
         lib.nbw_qgemm_grouped.restype = ctypes.c_int
         lib.nbw_unpack_codes.argtypes = [pv, i32, vp, vp]
@@ -199,28 +212,79 @@ def slice_view(w: PackedWeight, r: int) -> PackedWeight:
     return out
 
 
+def _need_rows(t: torch.Tensor, name: str, dtype, cols: int) -> None:
+    """A 2-d tensor whose rows are contiguous (row stride may exceed `cols`)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or t.shape[1] != cols or (t.shape[0] > 1 and t.stride(0) < cols) or \
+            (cols > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be [rows][{cols}] with unit column stride")
+
+
 def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
-          out: torch.Tensor | None = None, kernel: str = "auto") -> torch.Tensor:
-    """fp32 Y [B][n] = X . dequant_r(W)^T for the r-bit child of ``w``."""
-    _need(x, "x", torch.bfloat16, 2)
+          out: torch.Tensor | None = None, kernel: str = "auto", zeros: torch.Tensor | None = None,
+          out_dtype=torch.float32) -> torch.Tensor:
+    """Y [B][n] = X . dequant_r(W)^T for the r-bit child of ``w``.
+
+    ``x`` may have a row stride larger than k (e.g. a column slice of a wider
+    tensor), as may ``out``; ``zeros`` (bf16 [n][k/128]) selects asymmetric
+    children; ``out_dtype`` is torch.float32 or torch.bfloat16."""
     _need(scales, "scales", torch.bfloat16, 2)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-d tensor")
     b, k = x.shape
     if k != w.k:
         raise ValueError(f"x has k={k}, weights have k={w.k}")
+    _need_rows(x, "x", torch.bfloat16, k)
     if tuple(scales.shape) != (w.n, w.k // 128):
         raise ValueError(f"scales must be [{w.n}][{w.k // 128}], got {tuple(scales.shape)}")
     if scales.device != x.device or w.storage.device != x.device:
         raise ValueError("x, scales and weights must be on the same GPU")
+    if out_dtype not in Y_DTYPES:
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    if zeros is not None:
+        _need(zeros, "zeros", torch.bfloat16, 2)
+        if tuple(zeros.shape) != (w.n, w.k // 128) or zeros.device != x.device:
+            raise ValueError(f"zeros must be [{w.n}][{w.k // 128}] on the same GPU")
     if out is None:
-        out = torch.empty((b, w.n), dtype=torch.float32, device=x.device)
+        out = torch.empty((b, w.n), dtype=out_dtype, device=x.device)
     else:
-        _need(out, "out", torch.float32, 2)
-        if tuple(out.shape) != (b, w.n) or out.device != x.device:
+        _need_rows(out, "out", out_dtype, w.n)
+        if out.shape[0] != b or out.device != x.device:
             raise ValueError(f"out must be [{b}][{w.n}] on the same GPU")
-    _check(_lib().nbw_qgemm_kernel(ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(w.view),
-                                   ctypes.c_void_p(scales.data_ptr()), r,
-                                   ctypes.c_void_p(out.data_ptr()), KERNELS[kernel], _stream(x)),
+    opts = QgemmOpts(x.stride(0) if b > 1 else k, out.stride(0) if b > 1 else w.n,
+                     Y_DTYPES[out_dtype], KERNELS[kernel],
+                     zeros.data_ptr() if zeros is not None else None)
+    _check(_lib().nbw_qgemm_ex(ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(w.view),
+                               ctypes.c_void_p(scales.data_ptr()), r,
+                               ctypes.c_void_p(out.data_ptr()), ctypes.byref(opts), _stream(x)),
            "nbw_qgemm")
+    return out
+
+
+def choose_codes(w: torch.Tensor, scales: torch.Tensor, widths=(3, 4, 8),
+                 lambdas=(1.0, 1.0, 1.0)) -> torch.Tensor:
+    """Parent codes uint8 [n][k] for fp32 weights [n][k] (GPU): per weight, the
+    code minimising sum_t lambdas[t] * (w - dequant_{widths[t]}(code))^2."""
+    _need(w, "w", torch.float32, 2)
+    _need(scales, "scales", torch.bfloat16, 2)
+    n, k = w.shape
+    if tuple(scales.shape) != (n, k // 128) or k % 128:
+        raise ValueError(f"scales must be [{n}][{k // 128}] and k a multiple of 128")
+    widths = list(widths)
+    lambdas = list(lambdas)
+    if len(widths) != len(lambdas):
+        raise ValueError("widths and lambdas must have the same length")
+    wa = (ctypes.c_int32 * max(1, len(widths)))(*widths)
+    la = (ctypes.c_double * max(1, len(lambdas)))(*lambdas)
+    out = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    _check(_lib().nbw_choose_codes(ctypes.c_void_p(w.data_ptr()), n, k,
+                                   ctypes.c_void_p(scales.data_ptr()), wa, la, len(widths),
+                                   ctypes.c_void_p(out.data_ptr()), _stream(w)), "nbw_choose_codes")
     return out
 
 
@@ -320,6 +384,6 @@ def version() -> str:
     return _lib().nbw_version().decode()
 
 
-__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "unpack_codes", "plane_bytes",
+__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "choose_codes", "unpack_codes", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]

@@ -106,20 +106,29 @@ nbw_status nbw_slice_view(const nbw_wview *parent, int32_t r, nbw_wview *child) 
     return NBW_OK;
 }
 
-nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *w,
-                            const void *scales_bf16, int32_t r, float *y, nbw_kernel kernel,
-                            void *stream) {
+nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                        const void *scales_bf16, int32_t r, void *y, const nbw_qgemm_opts *opts,
+                        void *stream) {
+    nbw_qgemm_opts o = {};
+    if (opts) o = *opts;
     nbw_status st = check_view(w);
     if (st != NBW_OK) return st;
     if (batch < 0) return NBW_EINVAL;
     if (r < 1 || r > 8 || r > w->nplanes) return NBW_ERANGE;
-    if (kernel < NBW_KERNEL_AUTO || kernel > NBW_KERNEL_GEMM) return NBW_EUNSUPPORTED;
+    if (o.kernel < NBW_KERNEL_AUTO || o.kernel > NBW_KERNEL_GEMM) return NBW_EUNSUPPORTED;
+    if (o.y_dtype != NBW_Y_F32 && o.y_dtype != NBW_Y_BF16) return NBW_EUNSUPPORTED;
+    const int64_t ldx = o.ldx ? o.ldx : w->k, ldy = o.ldy ? o.ldy : w->n;
+    if (ldx < w->k || ldy < w->n) return NBW_EINVAL;
     if (batch == 0) return NBW_OK;  // empty product: nothing to read or write
     if (!x_bf16 || !scales_bf16 || !y) return NBW_EINVAL;
+    const bool ybf16 = o.y_dtype == NBW_Y_BF16;
     if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scales_bf16, 4)) return NBW_EALIGN;
+    if (o.zeros_bf16 && !aligned(o.zeros_bf16, 4)) return NBW_EALIGN;
+    if (ldx % 8 != 0) return NBW_EALIGN;  // X rows are read with 16-byte loads
     int cus = 0;
     st = cu_count(&cus);
     if (st != NBW_OK) return st;
+    int kernel = o.kernel;
     if (kernel == NBW_KERNEL_AUTO)
         kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
     nbw::QgemmArgs a;
@@ -130,13 +139,46 @@ nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *
     a.scales = (const uint16_t *)scales_bf16;
     a.n = (int)w->n;
     a.k = (int)w->k;
-    a.y = y;
+    a.y = (float *)y;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.ybf16 = ybf16 ? 1 : 0;
+    a.zeros = (const uint16_t *)o.zeros_bf16;
     hipError_t e;
     switch (kernel) {
     case NBW_KERNEL_GEMV: e = nbw::launch_gemv(r, a, cus, (hipStream_t)stream); break;
     case NBW_KERNEL_SMALLB: e = nbw::launch_smallb(r, a, cus, (hipStream_t)stream); break;
     default: e = nbw::launch_gemm(r, a, cus, (hipStream_t)stream); break;
     }
+    return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                            const void *scales_bf16, int32_t r, float *y, nbw_kernel kernel,
+                            void *stream) {
+    nbw_qgemm_opts o = {};
+    o.kernel = kernel;
+    return nbw_qgemm_ex(x_bf16, batch, w, scales_bf16, r, y, &o, stream);
+}
+
+nbw_status nbw_choose_codes(const float *w, int64_t n, int64_t k, const void *scales_bf16,
+                            const int32_t *widths, const double *lambdas, int32_t nw,
+                            uint8_t *codes_out, void *stream) {
+    if (!w || !scales_bf16 || !codes_out || !widths || !lambdas) return NBW_EINVAL;
+    if (!shape_ok(n, k)) return NBW_EINVAL;
+    if (nw < 1 || nw > 8) return NBW_EINVAL;
+    nbw::ChooseSpec spec = {};
+    spec.nw = nw;
+    for (int t = 0; t < nw; ++t) {
+        if (widths[t] < 1 || widths[t] > 8) return NBW_ERANGE;
+        // lambdas must be finite and >= 0 (this also rejects NaN)
+        if (!(lambdas[t] >= 0.0 && lambdas[t] <= 1.7976931348623157e308)) return NBW_EINVAL;
+        spec.widths[t] = widths[t];
+        spec.lambdas[t] = lambdas[t];
+    }
+    if (!aligned(w, 4) || !aligned(scales_bf16, 2)) return NBW_EALIGN;
+    hipError_t e = nbw::launch_choose(w, n, (int)k, (const uint16_t *)scales_bf16, spec, codes_out,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? NBW_OK : hip_failed(e);
 }
 

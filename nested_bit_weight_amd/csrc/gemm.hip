@@ -57,14 +57,18 @@ __device__ __forceinline__ f32x16_t gm_mfma(const u32x4_t &a, const u32x4_t &b, 
 
 // grid: (ceil(n / 256), ceil(batch / 128), splits); block 512.  Groups
 // [z * gps, min(G, (z + 1) * gps)) of k.  With atomic != 0 the result is added
-// to y (which the launcher has cleared); otherwise it is stored.
-template <int R>
+// to y (fp32, which the launcher has cleared); otherwise it is stored.  ASYM:
+// asymmetric children, zeros bf16 [n][k/128]: each weight gains
+// s * (127.5 - z) over the symmetric child, i.e. every chain starts from
+// correction + (127.5 - z) * 2^(R-8) * (group sum of the batch row's X).
+template <int R, bool ASYM>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
-    const uint16_t *__restrict__ x, int batch, const uint8_t *__restrict__ planes,
-    int64_t plane_bytes, const uint16_t *__restrict__ scales, int n, int k, int gps,
-    float *__restrict__ y, int atomic) {
+    const uint16_t *__restrict__ x, int64_t ldx, int batch, const uint8_t *__restrict__ planes,
+    int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    int n, int k, int gps, float *__restrict__ y, int64_t ldy, int ybf16, int atomic) {
     __shared__ __align__(16) uint16_t xs[2][GEMM_BM * GEMM_XSTRIDE];
     __shared__ __align__(16) float corr[2][GEMM_BM];
+    __shared__ __align__(16) float xsum[ASYM ? 2 : 1][GEMM_BM];
     constexpr int NPH = Phases<R>::count;
 
     const int G = k >> 7;
@@ -84,11 +88,12 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     const int rc = min(nrow, npad - 1);
     const uint8_t *pbase = planes + ((int64_t)(rc >> 4) * G * 16 + (rc & 15)) * 16 + 8 * h;
     const uint16_t *sbase = scales + (int64_t)min(nrow, n - 1) * G;
+    const uint16_t *zbase = ASYM ? zeros + (int64_t)min(nrow, n - 1) * G : nullptr;
 
     // X staging: thread (xr, qq) moves columns 32qq .. 32qq+31 (word qq of the
     // group: bf16 pairs m = 0..15) of batch row b0 + xr.
     const int xr = tid >> 2, qq = tid & 3;
-    const uint16_t *xrow = x + (int64_t)min(b0 + xr, batch - 1) * k + 32 * qq;
+    const uint16_t *xrow = x + (int64_t)min(b0 + xr, batch - 1) * ldx + 32 * qq;
     u32x4_t xv[4];
     auto load_x = [&](int g) {
 #pragma unroll
@@ -109,11 +114,24 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
         part += __shfl_xor(part, 1);
         part += __shfl_xor(part, 2);
         if (qq == 0) corr[buf][xr] = part;
+        if constexpr (ASYM) {
+            float sx = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                sx = gm_dot2(one, xv[c].x, sx);
+                sx = gm_dot2(one, xv[c].y, sx);
+                sx = gm_dot2(one, xv[c].z, sx);
+                sx = gm_dot2(one, xv[c].w, sx);
+            }
+            sx += __shfl_xor(sx, 1);
+            sx += __shfl_xor(sx, 2);
+            if (qq == 0) xsum[buf][xr] = sx;
+        }
     };
 
     // Planes and scale of groups g (cur) and g + 1 (next).
     u32x2_t pw[2][R];
-    uint32_t sraw[2];
+    uint32_t sraw[2], zraw[2];
     auto load_w = [&](int slot, int g) {
         const uint8_t *c = pbase + (int64_t)g * 256;
 #pragma unroll
@@ -121,6 +139,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
             pw[slot][p] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x2_t *>(c + (int64_t)p * plane_bytes));
         sraw[slot] = sbase[g];
+        if constexpr (ASYM) zraw[slot] = zbase[g];
     };
 
     load_x(g_begin);
@@ -154,11 +173,15 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
             }
         }
         const float s = nrow < n ? __uint_as_float(sraw[0] << 16) : 0.f;
+        const float zc = ASYM ? (127.5f - __uint_as_float(zraw[0] << 16)) *
+                                    (1.0f / (float)(1 << (8 - R)))
+                              : 0.f;
 
         // Shift the plane window and fetch two groups ahead; X one ahead.
 #pragma unroll
         for (int p = 0; p < R; ++p) pw[0][p] = pw[1][p];
         sraw[0] = sraw[1];
+        if constexpr (ASYM) zraw[0] = zraw[1];
         if (g + 2 < g_end) load_w(1, g + 2);
         const bool more = g + 1 < g_end;
         if (more) load_x(g + 1);
@@ -173,8 +196,14 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
                 const int bb = 2 * bp + e;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 c4 =
+                    float4 c4 =
                         *reinterpret_cast<const float4 *>(&corr[buf][32 * bb + 8 * q + 4 * h]);
+                    if constexpr (ASYM) {
+                        const float4 x4 =
+                            *reinterpret_cast<const float4 *>(&xsum[buf][32 * bb + 8 * q + 4 * h]);
+                        c4.x = fmaf(zc, x4.x, c4.x); c4.y = fmaf(zc, x4.y, c4.y);
+                        c4.z = fmaf(zc, x4.z, c4.z); c4.w = fmaf(zc, x4.w, c4.w);
+                    }
                     Pc[e][4 * q] = c4.x; Pc[e][4 * q + 1] = c4.y;
                     Pc[e][4 * q + 2] = c4.z; Pc[e][4 * q + 3] = c4.w;
                 }
@@ -213,21 +242,23 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int b = b0 + 32 * bb + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (b >= batch) continue;
-                float *dst = y + (int64_t)b * n + nrow;
+                const int64_t idx = (int64_t)b * ldy + nrow;
                 const float val = acc[bb][v] * post;
                 if (atomic)
-                    __hip_atomic_fetch_add(dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(y + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else
-                    *dst = val;
+                    store_y(y, ybf16, idx, val);
             }
     }
 }
 
-// Clears y before a split-k launch adds its partial sums.
-__global__ void gemm_zero_kernel(float *__restrict__ y, int64_t count) {
+// Clears the fp32 rows y[b][0..n) (row stride ldy) before a split-k launch
+// adds its partial sums.
+__global__ void gemm_zero_kernel(float *__restrict__ y, int64_t batch, int n, int64_t ldy) {
+    const int64_t count = batch * (int64_t)n;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = i; e < count; e += stride) y[e] = 0.f;
+    for (int64_t e = i; e < count; e += stride) y[(e / n) * ldy + e % n] = 0.f;
 }
 
 // Split k only when the output tiles leave most CUs idle; each split keeps
@@ -243,18 +274,25 @@ static int gemm_splits(const QgemmArgs &a, int cu_count) {
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int G = a.k / 128;
-    const int splits = gemm_splits(a, cu_count);
+    // split-k adds fp32 partial sums into y: only for fp32 outputs
+    const int splits = a.ybf16 ? 1 : gemm_splits(a, cu_count);
     const int gps = (G + splits - 1) / splits;
     if (splits > 1) {
         const int64_t count = a.batch * (int64_t)a.n;
         const int64_t blocks = (count + 255) / 256;
         hipLaunchKernelGGL(gemm_zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
-                           dim3(256), 0, stream, a.y, count);
+                           dim3(256), 0, stream, a.y, a.batch, a.n, a.ldy);
     }
     const dim3 grid((a.n + GEMM_BN - 1) / GEMM_BN, (unsigned)((a.batch + GEMM_BM - 1) / GEMM_BM),
                     splits);
-    hipLaunchKernelGGL(gemm_kernel<R>, grid, dim3(64 * GEMM_WAVES), 0, stream, a.x, (int)a.batch, a.planes,
-                       a.plane_bytes, a.scales, a.n, a.k, gps, a.y, splits > 1 ? 1 : 0);
+    if (a.zeros)
+        hipLaunchKernelGGL((gemm_kernel<R, true>), grid, dim3(64 * GEMM_WAVES), 0, stream, a.x,
+                           a.ldx, (int)a.batch, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k,
+                           gps, a.y, a.ldy, a.ybf16, splits > 1 ? 1 : 0);
+    else
+        hipLaunchKernelGGL((gemm_kernel<R, false>), grid, dim3(64 * GEMM_WAVES), 0, stream, a.x,
+                           a.ldx, (int)a.batch, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k,
+                           gps, a.y, a.ldy, a.ybf16, splits > 1 ? 1 : 0);
 }
 
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {
@@ -273,9 +311,8 @@ hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stre
 }
 
 void gemm_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
-    (void)a;
     (void)cu_count;
-    snprintf(out, len, "nbw::gemm_kernel<%d>", r);
+    snprintf(out, len, "nbw::gemm_kernel<%d, %s>", r, a.zeros ? "true" : "false");
 }
 
 }  // namespace nbw

@@ -67,13 +67,14 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // stream), stages it in its own 1 KB of LDS and reads back its lanes'
 // groups, so no barrier -- and no wait for every load in flight -- stands
 // between a wave's first loads and its first step.
-template <int R, int PD>
+template <int R, int PD, bool ASYM>
 __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
                                            const uint8_t *__restrict__ planes,
                                            int64_t plane_bytes,
-                                           const uint16_t *__restrict__ scales, int n, int k,
+                                           const uint16_t *__restrict__ scales,
+                                           const uint16_t *__restrict__ zeros, int n, int k,
                                            int t_begin, int T, int slots, float *__restrict__ y,
-                                           unsigned char *lds) {
+                                           int ybf16, unsigned char *lds) {
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
     const int W = blockDim.x >> 6;
@@ -108,6 +109,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     u32x4_t buf[PD][R];
     u32x4_t xbuf[PD];
     uint32_t sbuf[PD];
+    uint32_t zbuf[ASYM ? PD : 1];
     int ps = 0, pt = 0;  // next step to prefetch
     const int xchunks = k >> 3;
     auto load_step = [&](int j) {
@@ -130,6 +132,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         const int row = min(16 * (t_begin + t) + i, n - 1);
         const int64_t idx = (int64_t)row * G + g;
         sbuf[j] = *reinterpret_cast<const uint32_t *>(scales + (idx & ~(int64_t)1));
+        if constexpr (ASYM) zbuf[j] = *reinterpret_cast<const uint32_t *>(zeros + (idx & ~(int64_t)1));
         if (++pt == T) {
             pt = 0;
             ++ps;
@@ -141,7 +144,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     }
 
     uint32_t X2[64];
-    float cg = 0.f;
+    float cg = 0.f, sg = 0.f;  // group correction; group sum of X (asymmetric term)
     int cs = 0, ct = 0;  // step being computed
     auto compute = [&](int j) {
         const int g = 4 * (w + cs * W) + gg;
@@ -166,6 +169,13 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
             v += __shfl_xor(v, 4);
             v += __shfl_xor(v, 8);
             cg = v;
+            if constexpr (ASYM) {
+                sx += __shfl_xor(sx, 1);
+                sx += __shfl_xor(sx, 2);
+                sx += __shfl_xor(sx, 4);
+                sx += __shfl_xor(sx, 8);
+                sg = sx;
+            }
         }
         // four independent dot2 chains (one per 32-column word) keep a wave's
         // dependent-issue latency off the critical path
@@ -189,6 +199,13 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         const int row = 16 * (t_begin + ct) + i;
         const uint32_t sbits = (g & 1) ? (sbuf[j] & 0xFFFF0000u) : (sbuf[j] << 16);
         const float s = (gvalid && row < n) ? __uint_as_float(sbits) : 0.f;
+        if constexpr (ASYM) {
+            // asymmetric child = symmetric child + s * (127.5 - z) per weight;
+            // in the units of P (which the epilogue scales by 2^(8-R)):
+            const uint32_t zbits = (g & 1) ? (zbuf[j] & 0xFFFF0000u) : (zbuf[j] << 16);
+            const float zc = (127.5f - __uint_as_float(zbits)) * (1.0f / (float)(1 << (8 - R)));
+            return s * fmaf(zc, sg, P + cg);
+        }
         return s * (P + cg);
     };
     // Accumulate into this lane's own LDS slot for the tile: an add that
@@ -230,7 +247,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
             sum += (slot[0] + slot[16]) + (slot[32] + slot[48]);
         }
         const int row = 16 * t_begin + e;
-        if (row < n) y[row] = sum * post;
+        if (row < n) store_y(y, ybf16, row, sum * post);
     }
 }
 
@@ -242,7 +259,9 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
                                                        const uint8_t *__restrict__ planes,
                                                        int64_t plane_bytes,
                                                        const uint16_t *__restrict__ scales,
-                                                       int n, int k, float *__restrict__ y) {
+                                                       const uint16_t *__restrict__ zeros,
+                                                       int n, int k, float *__restrict__ y,
+                                                       int ybf16) {
     __shared__ float red[GEMV_ODD_WAVES][16];
     const int G = k >> 7;
     const int W = blockDim.x >> 6;
@@ -279,9 +298,19 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
                 if constexpr (Phases<R>::count == 2) P = dot2(D1[m], X2[16 * d + m], P);
             }
         }
-        const uint32_t sb = (uint32_t)scales[(int64_t)min(row, n - 1) * G + gc] << 16;
+        const int64_t sidx = (int64_t)min(row, n - 1) * G + gc;
+        const uint32_t sb = (uint32_t)scales[sidx] << 16;
         const float s = (gvalid && row < n) ? __uint_as_float(sb) : 0.f;
-        acc = fmaf(s, P + correction<R, 64>(X2), acc);
+        float Pc = P + correction<R, 64>(X2);
+        if (zeros) {  // asymmetric: + (127.5 - z) * 2^(R-8) * sum of the group's X
+            const uint32_t one = 0x3F803F80u;
+            float sx = 0.f;
+#pragma unroll
+            for (int m = 0; m < 64; ++m) sx = dot2(one, X2[m], sx);
+            const float z = __uint_as_float((uint32_t)zeros[sidx] << 16);
+            Pc = fmaf((127.5f - z) * (1.0f / (float)(1 << (8 - R))), sx, Pc);
+        }
+        acc = fmaf(s, Pc, acc);
     }
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
@@ -291,22 +320,24 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
         float sum = 0.f;
         for (int ww = 0; ww < W; ++ww) sum += red[ww][threadIdx.x];
         if (16 * tile + (int)threadIdx.x < n)
-            y[16 * tile + threadIdx.x] = sum * (float)(1 << (8 - R));
+            store_y(y, ybf16, 16 * tile + threadIdx.x, sum * (float)(1 << (8 - R)));
     }
 }
 
-template <int R, int PD>
+template <int R, int PD, bool ASYM>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(const uint16_t *__restrict__ x,
                                                                   const uint8_t *__restrict__ planes,
                                                                   int64_t plane_bytes,
                                                                   const uint16_t *__restrict__ scales,
+                                                                  const uint16_t *__restrict__ zeros,
                                                                   int n, int k, int tiles_total,
                                                                   int tiles_per_wg,
-                                                                  float *__restrict__ y) {
+                                                                  float *__restrict__ y, int ybf16) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int t_begin = blockIdx.x * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    gemv_tiles<R, PD>(x, planes, plane_bytes, scales, n, k, t_begin, T, tiles_per_wg, y, lds);
+    gemv_tiles<R, PD, ASYM>(x, planes, plane_bytes, scales, zeros, n, k, t_begin, T, tiles_per_wg,
+                            y, ybf16, lds);
 }
 
 // ---------------------------------------------------------------- grouped launch
@@ -338,8 +369,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_group_kernel(GemvGro
     switch (J.r) {
 #define NBW_GEMV_CASE(RR)                                                                    \
     case RR:                                                                                 \
-        gemv_tiles<RR, gemv_depth(RR)>(J.x, J.planes, J.plane_bytes, J.scales, J.n, J.k, t_begin, \
-                                       T, grp.slots, J.y, lds);                              \
+        gemv_tiles<RR, gemv_depth(RR), false>(J.x, J.planes, J.plane_bytes, J.scales, nullptr,   \
+                                              J.n, J.k, t_begin, T, grp.slots, J.y, 0, lds);  \
         break;
         NBW_GEMV_CASE(1)
         NBW_GEMV_CASE(2)
@@ -379,26 +410,37 @@ static GemvPlan gemv_plan(int n, int k, int r, int cu_count) {
 
 static bool gemv_streamable(int k);
 
+template <int R, bool ASYM>
+static void launch_stream(const GemvPlan &p, int tiles, const QgemmArgs &a, const uint16_t *x,
+                          float *y, hipStream_t stream) {
+    const dim3 grid((tiles + p.tpw - 1) / p.tpw), block(64 * p.waves);
+    const size_t lds = gemv_lds_bytes(p.waves, p.tpw);
+    if (p.deep)
+        hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R), ASYM>), grid, block, lds, stream, x, a.planes,
+                           a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, p.tpw, y, a.ybf16);
+    else
+        hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT, ASYM>), grid, block, lds, stream, x,
+                           a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, p.tpw, y,
+                           a.ybf16);
+}
+
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int tiles = (a.n + 15) / 16;
     for (int64_t b = 0; b < a.batch; ++b) {  // one batch row per launch
+        const uint16_t *x = a.x + b * a.ldx;
+        // (y advances by ldy elements of the output type)
+        float *y = a.ybf16 ? reinterpret_cast<float *>(reinterpret_cast<uint16_t *>(a.y) + b * a.ldy)
+                           : a.y + b * a.ldy;
         if (!gemv_streamable(a.k)) {
             hipLaunchKernelGGL(gemv_odd_kernel<R>, dim3(tiles), dim3(64 * GEMV_ODD_WAVES), 0, stream,
-                               a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k,
-                               a.y + b * a.n);
+                               x, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, y, a.ybf16);
         } else {
             const GemvPlan p = gemv_plan(a.n, a.k, R, cu_count);
-            const dim3 grid((tiles + p.tpw - 1) / p.tpw), block(64 * p.waves);
-            const size_t lds = gemv_lds_bytes(p.waves, p.tpw);
-            if (p.deep)
-                hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R)>), grid, block, lds, stream,
-                                   a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k, tiles,
-                                   p.tpw, a.y + b * a.n);
+            if (a.zeros)
+                launch_stream<R, true>(p, tiles, a, x, y, stream);
             else
-                hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT>), grid, block, lds, stream,
-                                   a.x + b * a.k, a.planes, a.plane_bytes, a.scales, a.n, a.k, tiles,
-                                   p.tpw, a.y + b * a.n);
+                launch_stream<R, false>(p, tiles, a, x, y, stream);
         }
     }
 }
@@ -423,7 +465,8 @@ void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
         snprintf(out, len, "nbw::gemv_odd_kernel<%d>", r);
     } else {
         const GemvPlan p = gemv_plan(a.n, a.k, r, cu_count);
-        snprintf(out, len, "nbw::gemv_kernel<%d, %d>", r, p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT);
+        snprintf(out, len, "nbw::gemv_kernel<%d, %d, %s>", r, p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT,
+                 a.zeros ? "true" : "false");
     }
 }
 
@@ -433,7 +476,9 @@ int gemv_group_capacity() { return GEMV_MAX_GROUP; }
 // group counts (every other shape goes to the plain one-tile kernel).
 static bool gemv_streamable(int k) { return ((k / 128) & 1) == 0; }
 
-bool gemv_group_eligible(const QgemmArgs &a) { return a.batch == 1 && gemv_streamable(a.k); }
+bool gemv_group_eligible(const QgemmArgs &a) {
+    return a.batch == 1 && gemv_streamable(a.k) && !a.zeros && !a.ybf16;
+}
 
 hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
                              hipStream_t stream) {

@@ -10,17 +10,40 @@ namespace nbw {
 
 // Geometry shared by the qgemm launchers.
 struct QgemmArgs {
-    const uint16_t *x;       // bf16 [batch][k]
+    const uint16_t *x;       // bf16 [batch][ldx]
     int64_t batch;
     const uint8_t *planes;   // plane 0 of the child
     int64_t plane_bytes;
     const uint16_t *scales;  // bf16 [n][k/128]
     int n, k;
-    float *y;                // fp32 [batch][n]
+    float *y;                // fp32 [batch][ldy] (or bf16 when ybf16)
+    int64_t ldx = 0, ldy = 0;          // row strides in elements (set by the caller: >= k, >= n)
+    int ybf16 = 0;                     // store Y as bf16 (round to nearest even)
+    const uint16_t *zeros = nullptr;   // asymmetric: bf16 [n][k/128] zero points, else null
+};
+
+// Y element store shared by the kernels: fp32, or bf16 rounded to nearest even.
+__device__ __forceinline__ void store_y(float *y, int ybf16, int64_t idx, float v) {
+    if (ybf16) {
+        uint32_t u = __float_as_uint(v);
+        u += 0x7FFFu + ((u >> 16) & 1u);
+        reinterpret_cast<uint16_t *>(y)[idx] = (uint16_t)(u >> 16);
+    } else {
+        y[idx] = v;
+    }
+}
+
+// Widths and weights of the code-choice objective (at most 8 widths).
+struct ChooseSpec {
+    int widths[8];
+    double lambdas[8];
+    int nw;
 };
 
 hipError_t launch_pack(const uint8_t *codes, int n, int k, uint8_t *planes, int64_t plane_bytes,
                        hipStream_t stream);
+hipError_t launch_choose(const float *w, int64_t n, int k, const uint16_t *scales,
+                         const ChooseSpec &spec, uint8_t *codes, hipStream_t stream);
 hipError_t launch_unpack(int r, const uint8_t *planes, int64_t plane_bytes, int n, int k,
                          uint8_t *codes, hipStream_t stream);
 hipError_t launch_gemv(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);

@@ -33,11 +33,14 @@ __device__ __forceinline__ float sb_bf16_to_f32(uint16_t h) { return __uint_as_f
 
 template <int R, int TM>
 __global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict__ x, int64_t batch,
+                                                     int64_t ldx,
                                                      const uint8_t *__restrict__ planes,
                                                      int64_t plane_bytes,
-                                                     const uint16_t *__restrict__ scales, int n,
+                                                     const uint16_t *__restrict__ scales,
+                                                     const uint16_t *__restrict__ zeros, int n,
                                                      int k, int tiles_total,
-                                                     float *__restrict__ y) {
+                                                     float *__restrict__ y, int64_t ldy,
+                                                     int ybf16) {
     __shared__ float red[SMALLB_MAX_WAVES][TM][4][64];
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
@@ -60,13 +63,14 @@ __global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict_
         // columns 128g + 32d + 8j + 2e (+1) of batch row bcol.
         uint32_t XB[4][16];
         f32x4_t init[4];
+        float xsum[4];  // group sums of this batch row's X (asymmetric term)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const int g = 4 * set + gi;
             const bool ok = bvalid && g < G;
             const int gc = g < G ? g : G - 1;
             const u32x4_t *src =
-                reinterpret_cast<const u32x4_t *>(x + bclamp * k + 128 * gc + 32 * d);
+                reinterpret_cast<const u32x4_t *>(x + bclamp * ldx + 128 * gc + 32 * d);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4_t v = ok ? src[j] : u32x4_t{0u, 0u, 0u, 0u};
@@ -77,6 +81,19 @@ __global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict_
             corr += __shfl_xor(corr, 16);
             corr += __shfl_xor(corr, 32);
             init[gi] = f32x4_t{corr, corr, corr, corr};
+            xsum[gi] = 0.f;
+            if (zeros) {
+                const uint32_t one = 0x3F803F80u;
+                float sx = 0.f;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
+                                                         __builtin_bit_cast(bf16x2_t, XB[gi][m]),
+                                                         sx, false);
+                sx += __shfl_xor(sx, 16);
+                sx += __shfl_xor(sx, 32);
+                xsum[gi] = sx;
+            }
         }
 
         // Plane words: lane (c, d) reads word d of row c's chunk, per plane.
@@ -124,10 +141,15 @@ __global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict_
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int row = 16 * (tile0 + t) + 4 * d + v;
-                    float s = 0.f;
-                    if (g < G && t < tcount && row < n)
+                    float s = 0.f, pv = P[v];
+                    if (g < G && t < tcount && row < n) {
                         s = sb_bf16_to_f32(scales[(int64_t)row * G + g]);
-                    acc[t][v] = fmaf(s, P[v], acc[t][v]);
+                        if (zeros) {  // + (127.5 - z) * 2^(R-8) * group sum of X
+                            const float z = sb_bf16_to_f32(zeros[(int64_t)row * G + g]);
+                            pv = fmaf((127.5f - z) * (1.0f / (float)(1 << (8 - R))), xsum[gi], pv);
+                        }
+                    }
+                    acc[t][v] = fmaf(s, pv, acc[t][v]);
                 }
             }
         }
@@ -145,7 +167,7 @@ __global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict_
         for (int ww = 0; ww < W; ++ww) sum += red[ww][t][v][l];
         const int row = 16 * (tile0 + t) + 4 * (l >> 4) + v;
         const int64_t b = (int64_t)blockIdx.y * 16 + (l & 15);
-        if (t < tcount && row < n && b < batch) y[b * n + row] = sum * post;
+        if (t < tcount && row < n && b < batch) store_y(y, ybf16, b * ldy + row, sum * post);
     }
 }
 
@@ -154,7 +176,8 @@ static void launch_tm(const QgemmArgs &a, int waves, hipStream_t stream) {
     const int tiles = (a.n + 15) / 16;
     dim3 grid((unsigned)((tiles + TM - 1) / TM), (unsigned)((a.batch + 15) / 16));
     hipLaunchKernelGGL((smallb_kernel<R, TM>), grid, dim3(64 * waves), 0, stream, a.x, a.batch,
-                       a.planes, a.plane_bytes, a.scales, a.n, a.k, tiles, a.y);
+                       a.ldx, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, a.y,
+                       a.ldy, a.ybf16);
 }
 
 static int smallb_tm(const QgemmArgs &a, int cu_count) {

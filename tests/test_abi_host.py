@@ -129,3 +129,48 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         nbw.pack_bitplanes(torch.zeros((16, 128), dtype=torch.uint8))
+
+
+def test_qgemm_ex_validation(lib):
+    _, v = _view(lib, n=64, k=256)
+    p = ctypes.c_void_p
+
+    def call(opts=None, b=4, y=FAKE, x=FAKE):
+        o = None if opts is None else ctypes.byref(opts)
+        return lib.nbw_qgemm_ex(p(x), b, ctypes.byref(v), p(FAKE), 4, p(y), o, None)
+
+    def opts(**kw):
+        o = nbw.QgemmOpts()
+        for key, val in kw.items():
+            setattr(o, key, val)
+        return o
+
+    assert call(opts(ldx=255)) == EINVAL            # below k
+    assert call(opts(ldy=63)) == EINVAL             # below n
+    assert call(opts(ldx=260)) == EALIGN            # rows would lose 16-byte alignment
+    assert call(opts(y_dtype=2)) == EUNSUPPORTED
+    assert call(opts(kernel=9)) == EUNSUPPORTED
+    assert call(opts(zeros_bf16=FAKE + 2)) == EALIGN
+    assert call(opts(), b=0, x=0, y=0) == OK        # empty product
+
+
+def test_choose_codes_validation(lib):
+    p = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    dbl = ctypes.c_double
+
+    def call(widths, lambdas, n=16, k=128, w=FAKE):
+        wa = (i32 * max(1, len(widths)))(*widths)
+        la = (dbl * max(1, len(lambdas)))(*lambdas)
+        return lib.nbw_choose_codes(p(w), n, k, p(FAKE), wa, la, len(widths), p(FAKE), None)
+
+    assert call([], []) == EINVAL
+    assert call([3, 4, 8, 1, 2, 5, 6, 7, 8], [1.0] * 9) == EINVAL
+    assert call([9], [1.0]) == ERANGE
+    assert call([0], [1.0]) == ERANGE
+    assert call([8], [-1.0]) == EINVAL
+    assert call([8], [float("nan")]) == EINVAL
+    assert call([8], [float("inf")]) == EINVAL
+    assert call([8], [1.0], k=100) == EINVAL
+    assert call([8], [1.0], w=0) == EINVAL
+    assert call([8], [1.0], w=FAKE + 2) == EALIGN
