@@ -38,6 +38,9 @@ sys.path.insert(0, ROOT)
 METRIC = "sliced int-r qgemm GB/s (batch 1) and TFLOP/s (batch 256) vs roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# fp64 vector issue rate: 78.6 TFLOP/s counts an FMA as two; single fp64 ops
+# (add, mul) issue at half that many per second.
+FP64_OPS_PEAK_T = 39.3
 RS_B1 = (4, 3, 2)
 RS_B256 = (8, 4, 3, 2)
 CPU_SAMPLE_SECONDS = 12.0
@@ -420,9 +423,53 @@ def main():
         del codes, outs
         log(f"pack: {pack_gbs:.1f} GB/s")
 
+        # ---- variants (same batch-1 step): asymmetric children and bf16 outputs
+        wid = synth.WORKLOAD_IDS["llama3.1-8b"]
+        zrng = synth.rng_for(0, wid, 0, synth.T_WEIGHTS)
+        for L in layer.lin:
+            z = zrng.integers(96, 160, size=(L["n"], L["k"] // 128)).astype("float32")
+            L["z"] = torch.from_numpy(synth.f32_to_bf16_bits(z)).view(torch.bfloat16).cuda()
+            L["y1b"] = torch.empty((1, L["n"]), dtype=torch.bfloat16, device="cuda")
+
+        def variant_step(i, **kw):
+            for ri, r in enumerate(RS_B1):
+                c = copy_of(layer, RS_B1, i, ri)
+                for L in layer.lin:
+                    out = L["y1b"] if kw.get("out_dtype") is torch.bfloat16 else L["y1"]
+                    nbw.qgemm(L["x1"], L["w"][c].slice_view(r), L["s"][c], r, out=out,
+                              zeros=L["z"] if kw.get("asym") else None,
+                              out_dtype=kw.get("out_dtype", torch.float32))
+        variants = {}
+        for name, kw in (("asymmetric", {"asym": True}), ("bf16_out", {"out_dtype": torch.bfloat16})):
+            gr = [capture(torch, lambda j=j, kw=kw: variant_step(j, **kw)) for j in range(layer.copies)]
+            for i in range(5):
+                gr[i % layer.copies].replay()
+            vms = event_time(torch, lambda i: gr[(5 + i) % layer.copies].replay(), max(10, args.steps // 4))
+            variants[name] = {"GBps": round(bytes_step / (vms * 1e-3) / 1e9, 1), "ms_per_step": round(vms, 5)}
+            del gr
+            log(f"batch 1 {name}: {variants[name]['GBps']} GB/s")
+        result["variants_b1"] = variants
+
+        # ---- data-free parent-code choice (offline, like pack): weights per second on the
+        # gate_up matrix, fp64 brute force over 256 codes x widths (3, 4, 8)
+        Lg = [L for L in layer.lin if L["name"] == "gate_up"][0]
+        gen = torch.Generator(device="cuda").manual_seed(0)
+        wf = torch.randn((Lg["n"], Lg["k"]), device="cuda", generator=gen) * 0.02  # N(0, 0.02) weights
+        nbw.choose_codes(wf, Lg["s"][0])
+        cms = event_time(torch, lambda i: nbw.choose_codes(wf, Lg["s"][0]), 3)
+        nweights = Lg["n"] * Lg["k"]
+        ops = nweights * 256 * 3 * 8  # fp64 operations per weight: 256 codes x 3 widths x 8
+        result["choose_codes"] = {
+            "weights_per_s": round(nweights / (cms * 1e-3), 1), "ms": round(cms, 3),
+            "shape": [Lg["n"], Lg["k"]], "widths": [3, 4, 8],
+            "roofline": {"bound": "alu", "achieved": round(ops / (cms * 1e-3) / 1e12, 2),
+                         "peak": FP64_OPS_PEAK_T, "unit": "T fp64 op/s",
+                         "frac": round(ops / (cms * 1e-3) / 1e12 / FP64_OPS_PEAK_T, 4)}}
+        del wf
+        log(f"choose_codes: {cms:.2f} ms for {nweights} weights")
+
         # ---- batch 4 and 16 (same linears, same recipe)
         other = {}
-        wid = synth.WORKLOAD_IDS["llama3.1-8b"]
         for b in (4, 16):
             for sid, L in enumerate(layer.lin):
                 xb = synth.activations(b, L["k"], synth.rng_for(0, wid, sid, synth.T_X))
