@@ -22,14 +22,17 @@
 //    buffered, rows padded against bank conflicts): lane (row l%32, half h)
 //    reads the same 8 columns 64h + 8j .. +7, so the k order of both
 //    operands agrees.
-//  - every 8-MFMA chain covers one group and starts from the group's
-//    correction (sum_k x_k * (1/2 - 2^(r-1) - offset_k), X only); the group
+//  - every 8-MFMA chain covers one group and starts from zero; the group
 //    scale, one per lane (lane = weight row), is folded in fp32 right after.
 //    Two batch blocks run their chains interleaved, so no MFMA waits on the
 //    one before it.
+//  - the decode's constant offsets leave a per-group correction
+//    sum_k x_k * (1/2 - 2^(r-1) - offset_k) (X only) times the group scale;
+//    these enter as a small fp32 product over groups (v_mfma_f32_32x32x2_f32,
+//    two groups per instruction) from a four-slot LDS ring.
 //  - X is loaded one group ahead (thread (row, quarter) moves 32 columns
-//    and forms their share of the row's correction), planes and scales two
-//    groups ahead; one barrier per group hands the X buffers over.
+//    and forms their share of the row's correction), planes and scales one
+//    group ahead too; one barrier per group hands the X buffers over.
 #include <cstdio>
 
 #include "decode.h"
@@ -59,16 +62,19 @@ __device__ __forceinline__ f32x16_t gm_mfma(const u32x4_t &a, const u32x4_t &b, 
 // [z * gps, min(G, (z + 1) * gps)) of k.  With atomic != 0 the result is added
 // to y (fp32, which the launcher has cleared); otherwise it is stored.  ASYM:
 // asymmetric children, zeros bf16 [n][k/128]: each weight gains
-// s * (127.5 - z) over the symmetric child, i.e. every chain starts from
-// correction + (127.5 - z) * 2^(R-8) * (group sum of the batch row's X).
+// s * (127.5 - z) over the symmetric child, i.e. the product gains
+// s * (127.5 - z) * 2^(R-8) * (group sum of the batch row's X), added through
+// the same fp32 product as the corrections.
 template <int R, bool ASYM>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int batch, const uint8_t *__restrict__ planes,
     int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     int n, int k, int gps, float *__restrict__ y, int64_t ldy, int ybf16, int atomic) {
     __shared__ __align__(16) uint16_t xs[2][GEMM_BM * GEMM_XSTRIDE];
-    __shared__ __align__(16) float corr[2][GEMM_BM];
-    __shared__ __align__(16) float xsum[ASYM ? 2 : 1][GEMM_BM];
+    // corrections (and group sums of X) of the last four groups, per batch row:
+    // while group g runs, the pair (g-2, g-1) is read and g+1 is staged
+    __shared__ __align__(16) float corr[4][GEMM_BM];
+    __shared__ __align__(16) float xsum[ASYM ? 4 : 1][GEMM_BM];
     constexpr int NPH = Phases<R>::count;
 
     const int G = k >> 7;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
         for (int c = 0; c < 4; ++c)
             xv[c] = *reinterpret_cast<const u32x4_t *>(xrow + 128 * g + 8 * c);
     };
-    auto stage_x = [&](int buf) {
+    auto stage_x = [&](int buf, int slot) {
         const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
         float part = 0.f;
 #pragma unroll
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
         }
         part += __shfl_xor(part, 1);
         part += __shfl_xor(part, 2);
-        if (qq == 0) corr[buf][xr] = part;
+        if (qq == 0) corr[slot][xr] = part;
         if constexpr (ASYM) {
             float sx = 0.f;
 #pragma unroll
@@ -125,27 +131,28 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
             }
             sx += __shfl_xor(sx, 1);
             sx += __shfl_xor(sx, 2);
-            if (qq == 0) xsum[buf][xr] = sx;
+            if (qq == 0) xsum[slot][xr] = sx;
         }
     };
 
-    // Planes and scale of groups g (cur) and g + 1 (next).
-    u32x2_t pw[2][R];
-    uint32_t sraw[2], zraw[2];
-    auto load_w = [&](int slot, int g) {
+    // Planes and scale of the next group to decode.  They are reloaded right
+    // after each decode (one group ahead), so no register copy -- which
+    // would wait for the load it copies -- is ever needed.
+    u32x2_t pw[R];
+    uint32_t sraw, zraw;
+    auto load_w = [&](int g) {
         const uint8_t *c = pbase + (int64_t)g * 256;
 #pragma unroll
         for (int p = 0; p < R; ++p)
-            pw[slot][p] = __builtin_nontemporal_load(
+            pw[p] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x2_t *>(c + (int64_t)p * plane_bytes));
-        sraw[slot] = sbase[g];
-        if constexpr (ASYM) zraw[slot] = zbase[g];
+        sraw = sbase[g];
+        if constexpr (ASYM) zraw = zbase[g];
     };
 
     load_x(g_begin);
-    load_w(0, g_begin);
-    if (g_begin + 1 < g_end) load_w(1, g_begin + 1);
-    stage_x(0);
+    load_w(g_begin);
+    stage_x(0, 0);
     __syncthreads();
 
     f32x16_t acc[4];
@@ -154,8 +161,32 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[bb][v] = 0.f;
 
+    // The corrections enter through the fp32 matrix path, not the chains:
+    // sum_g s[n][g] * corr[b][g] (and, asymmetric, sum_g s*zc[n][g] * xsum[b][g])
+    // is a product over groups, added into acc two groups at a time with
+    // v_mfma_f32_32x32x2_f32 (A: corrections [batch row][group], B: scales
+    // [group][weight row]); lane half h takes the pair's group h.
+    // (all reads first, then the MFMAs: one wait for the four reads)
+    auto correct = [&](int slot_h, float bv, float bv2) {
+        float a[4], a2[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            a[bb] = corr[slot_h][32 * bb + l32];
+            if constexpr (ASYM) a2[bb] = xsum[slot_h][32 * bb + l32];
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            acc[bb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[bb], bv, acc[bb], 0, 0, 0);
+            if constexpr (ASYM)
+                acc[bb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[bb], bv2, acc[bb], 0, 0, 0);
+        }
+    };
+    // scales (and scale * zc) of the last two groups, for their pair's correction
+    float s_prev = 0.f, zs_prev = 0.f, s_prev2 = 0.f, zs_prev2 = 0.f;
+
     for (int g = g_begin; g < g_end; ++g) {
         const int buf = (g - g_begin) & 1;
+        const int slot = (g - g_begin) & 3;
 
         // Decode this group's weight operands: Bop[ph][pair].
         uint32_t Bop[NPH][32];
@@ -163,7 +194,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
         for (int q = 0; q < 2; ++q) {
             uint32_t P[R];
 #pragma unroll
-            for (int p = 0; p < R; ++p) P[p] = q ? pw[0][p].y : pw[0][p].x;
+            for (int p = 0; p < R; ++p) P[p] = q ? pw[p].y : pw[p].x;
             uint32_t D0[16], D1[16];
             decode_word<R>(P, D0, D1);
 #pragma unroll
@@ -172,42 +203,33 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
                 if constexpr (NPH == 2) Bop[NPH - 1][16 * q + m] = D1[m];
             }
         }
-        const float s = nrow < n ? __uint_as_float(sraw[0] << 16) : 0.f;
-        const float zc = ASYM ? (127.5f - __uint_as_float(zraw[0] << 16)) *
+        const float s = nrow < n ? __uint_as_float(sraw << 16) : 0.f;
+        const float zc = ASYM ? (127.5f - __uint_as_float(zraw << 16)) *
                                     (1.0f / (float)(1 << (8 - R)))
                               : 0.f;
+        // Groups g-2, g-1 form a finished pair: their corrections go in now,
+        // next to this group's decode (their slots are not written again
+        // before the barrier after group g+1).
+        if (g - g_begin >= 2 && ((g - g_begin) & 1) == 0)
+            correct(h ? (slot + 3) & 3 : (slot + 2) & 3, h ? s_prev : s_prev2, h ? zs_prev : zs_prev2);
 
-        // Shift the plane window and fetch two groups ahead; X one ahead.
-#pragma unroll
-        for (int p = 0; p < R; ++p) pw[0][p] = pw[1][p];
-        sraw[0] = sraw[1];
-        if constexpr (ASYM) zraw[0] = zraw[1];
-        if (g + 2 < g_end) load_w(1, g + 2);
-        const bool more = g + 1 < g_end;
-        if (more) load_x(g + 1);
+        // Fetch X and the planes of the next group.  X goes first: loads
+        // retire in order, so staging X then waits only for X (an L2 hit),
+        // not for the planes coming from HBM.  The loads are unconditional
+        // (clamped to the last group), so the number in flight behind X is
+        // static and the compiler's wait for X stays exact.
+        const int gn = min(g + 1, g_end - 1);
+        load_x(gn);
+        load_w(gn);
 
 #pragma unroll
         for (int bp = 0; bp < 2; ++bp) {
-            // Two batch blocks, chains interleaved; each starts from the
-            // correction of its batch rows.
+            // Two batch blocks, chains interleaved, each from zero.
             f32x16_t Pc[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int bb = 2 * bp + e;
+            for (int e = 0; e < 2; ++e)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float4 c4 =
-                        *reinterpret_cast<const float4 *>(&corr[buf][32 * bb + 8 * q + 4 * h]);
-                    if constexpr (ASYM) {
-                        const float4 x4 =
-                            *reinterpret_cast<const float4 *>(&xsum[buf][32 * bb + 8 * q + 4 * h]);
-                        c4.x = fmaf(zc, x4.x, c4.x); c4.y = fmaf(zc, x4.y, c4.y);
-                        c4.z = fmaf(zc, x4.z, c4.z); c4.w = fmaf(zc, x4.w, c4.w);
-                    }
-                    Pc[e][4 * q] = c4.x; Pc[e][4 * q + 1] = c4.y;
-                    Pc[e][4 * q + 2] = c4.z; Pc[e][4 * q + 3] = c4.w;
-                }
-            }
+                for (int v = 0; v < 16; ++v) Pc[e][v] = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
 #pragma unroll
@@ -229,8 +251,23 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
                 for (int v = 0; v < 16; ++v) acc[2 * bp + e][v] = fmaf(s, Pc[e][v], acc[2 * bp + e][v]);
         }
 
-        if (more) stage_x(buf ^ 1);
+        s_prev2 = s_prev;
+        zs_prev2 = zs_prev;
+        s_prev = s;
+        zs_prev = ASYM ? s * zc : 0.f;
+
+        stage_x(buf ^ 1, (slot + 1) & 3);  // (past the end: a repeat of the last group, never read)
         __syncthreads();
+    }
+    // The last pair, or an unpaired last group through the h = 0 lanes (the
+    // h = 1 lanes multiply a valid correction by zero).
+    {
+        const int ng = g_end - g_begin;
+        const int last = (ng - 1) & 3;
+        if (ng & 1)
+            correct(last, h ? 0.f : s_prev, h ? 0.f : zs_prev);
+        else
+            correct(h ? last : (last + 3) & 3, h ? s_prev : s_prev2, h ? zs_prev : zs_prev2);
     }
 
     // Epilogue: lane holds rows b0 + 32bb + 8(v/4) + 4h + v%4 of column nrow.

@@ -5,8 +5,9 @@
   127.5 they must equal the symmetric kernels bit for bit (the asymmetric
   term is then an exact zero);
 * bf16 outputs: |Y - R| <= 2^-8 |R| + 2e-3 max|R| per batch row (the output
-  rounding plus the fp32 contract), and exactly the fp32 result rounded to
-  nearest even;
+  rounding plus the fp32 contract), and the fp32 result of the same kernel
+  rounded to nearest even (exactly, where both launches sum in the same
+  order);
 * strided X and Y (row strides above k and n) give bit-identical results to
   dense operands and leave the gaps between rows untouched;
 * the code chooser is bit-exact against the oracle's brute force.
@@ -105,8 +106,14 @@ def test_bf16_output(nbw, kernel, r):
     torch.cuda.synchronize()
     assert y16.dtype == torch.bfloat16
     got = y16.float().cpu().numpy().astype(np.float64)
-    # exactly the fp32 result rounded to nearest even
-    assert np.array_equal(got, bf16_round(y32.cpu().numpy()))
+    f32 = y32.cpu().numpy()
+    if kernel == "gemm":
+        # the fp32 launch may split k (atomic partial sums) where the bf16 one
+        # does not: same value up to fp32 rounding, so within one bf16 rounding
+        assert np.all(np.abs(got - f32) <= 2.0 ** -8 * np.abs(f32) + 1e-6 * np.abs(f32).max())
+    else:
+        # exactly the fp32 result rounded to nearest even
+        assert np.array_equal(got, bf16_round(f32))
     ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, r)
     bound = 2.0 ** -8 * np.abs(ref) + CONTRACT * np.abs(ref).max(axis=1, keepdims=True)
     assert np.all(np.abs(got - ref) <= bound)
