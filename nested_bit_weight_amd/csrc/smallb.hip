@@ -4,7 +4,8 @@
 // Nested Quantized Models, Abstract: kernels supporting batch sizes beyond
 // one; Figure 1: batch sweep), for 2..16 batch rows per launch slice.  Beyond
 // one batch row the bf16 dot products would take more VALU issue slots than
-// the plane decode itself, so the contraction moves to the matrix cores:
+// the plane decode itself, so the contraction moves to the matrix cores; the
+// product is still bound by HBM, so the kernel streams like the batch-1 one:
 //
 //  - one v_mfma_f32_16x16x32_bf16 multiplies a 16-row x 32-column weight
 //    fragment by 32 columns of up to 16 batch rows.  Lane l supplies row l%16,
@@ -15,11 +16,18 @@
 //  - lane (row c, quarter d) of a wave loads 32-bit word d of its row's
 //    16-byte chunk of each plane: one wave load covers the 256 contiguous
 //    bytes of a 16-row tile of one group.
-//  - every MFMA chain covers one 128-wide group, so the group scale is folded
-//    in fp32 right after it (one FMA per output); the chain starts from the
-//    correction that removes the decoded operands' constant offsets.
-//  - a wave keeps the activation operands of its 4-group set in registers
-//    and walks the tiles of its workgroup; waves split k and meet in LDS.
+//  - a workgroup owns a run of T 16-row tiles and all of k (about one
+//    workgroup per CU); its waves split k into 4-group sets (wave w: sets w,
+//    w+W, ...).  For each of its sets a wave loads the set's activation
+//    operands (16 batch rows x 512 columns, 64 registers per lane), then
+//    walks the T tiles with PD tiles of planes and scales in flight.  The
+//    loads inside a set are unconditional (clamped at the end), so the loads
+//    in flight between a load and its use are a static count.
+//  - every MFMA chain covers one 128-wide group and starts from the
+//    correction that removes the decoded operands' constant offsets; the
+//    group scale is folded in fp32 right after it (one FMA per output).
+//  - each lane adds its four outputs of a step to its own LDS slot for the
+//    tile (an add that returns nothing); the waves meet there at the end.
 #include <cstdio>
 
 #include "decode.h"
@@ -27,175 +35,262 @@
 
 namespace nbw {
 
-constexpr int SMALLB_MAX_WAVES = 8;
+constexpr int SMALLB_WAVES = 8;      // waves per workgroup
+constexpr int SMALLB_MAX_TILES = 16; // tiles per workgroup
+constexpr int SMALLB_DEPTH = 2;      // steps of planes in flight per wave
 
-__device__ __forceinline__ float sb_bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float sb_bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-template <int R, int TM>
-__global__ __launch_bounds__(512) void smallb_kernel(const uint16_t *__restrict__ x, int64_t batch,
-                                                     int64_t ldx,
-                                                     const uint8_t *__restrict__ planes,
-                                                     int64_t plane_bytes,
-                                                     const uint16_t *__restrict__ scales,
-                                                     const uint16_t *__restrict__ zeros, int n,
-                                                     int k, int tiles_total,
-                                                     float *__restrict__ y, int64_t ldy,
-                                                     int ybf16) {
-    __shared__ float red[SMALLB_MAX_WAVES][TM][4][64];
+// Dynamic LDS: fp32 [W][T][4][64] partial sums (tile t, output v of lane l).
+__host__ __device__ constexpr size_t smallb_lds_bytes(int waves, int slots) {
+    return (size_t)waves * slots * 4 * 64 * 4;
+}
+
+// grid: (ceil(tiles / tiles_per_wg), ceil(batch / 16)); block 64 * SMALLB_WAVES.
+// S4: k/128 is a multiple of 4, so the scales (and zero points) of a row's
+// four groups of a set are one aligned 8-byte word.
+template <int R, int PD, bool ASYM, bool S4>
+__global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
+    const uint16_t *__restrict__ x, int64_t batch, int64_t ldx, const uint8_t *__restrict__ planes,
+    int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    int n, int k, int tiles_total, int tiles_per_wg, float *__restrict__ y, int64_t ldy,
+    int ybf16) {
+    extern __shared__ __align__(16) float red[];  // [W][tiles_per_wg][4][64]
+    constexpr int NPH = Phases<R>::count;
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
-    const int W = blockDim.x >> 6;
-    const int w = threadIdx.x >> 6;
+    const int W = SMALLB_WAVES;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, d = lane >> 4;
-    const int tile0 = blockIdx.x * TM;
-    const int tcount = min(TM, tiles_total - tile0);
+    const int t_begin = blockIdx.x * tiles_per_wg;
+    const int T = min(tiles_per_wg, tiles_total - t_begin);
     const int64_t bcol = (int64_t)blockIdx.y * 16 + c;
     const bool bvalid = bcol < batch;
     const int64_t bclamp = bvalid ? bcol : batch - 1;
 
-    f32x4_t acc[TM];
+    // This wave's sets: ordinal s = 0 .. my_sets-1 is set w + s*W.
+    const int my_sets = nsets > w ? (nsets - w + W - 1) / W : 0;
+    float *slot = red + (size_t)w * tiles_per_wg * 256;
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int t = 0; t < TM; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < 4; ++v) slot[(t * 4 + v) * 64 + lane] = 0.f;
 
-    for (int set = w; set < nsets; set += W) {
-        // Activation operands of the 4 groups: XB[gi][4j+e] is the bf16 pair of
-        // columns 128g + 32d + 8j + 2e (+1) of batch row bcol.
-        uint32_t XB[4][16];
-        f32x4_t init[4];
-        float xsum[4];  // group sums of this batch row's X (asymmetric term)
+    // Step loads: for each of the set's 4 groups, the lane's plane words;
+    // for each of the lane's 4 output rows (4d + v), the scales (and zero
+    // points) of the 4 groups.
+    uint32_t pl[PD][4][R];
+    uint32_t sw[PD][4][2];
+    uint32_t zw[ASYM ? PD : 1][4][2];
+    auto load_step = [&](int j, int set, int t) {
+        const int tile = t_begin + min(t, T - 1);
+        // (scales first: loads retire in issue order, and the plane words,
+        // used first, should not be the last ones issued)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = min(16 * tile + 4 * d + v, n - 1);
+            if constexpr (S4) {
+                const int64_t idx = (int64_t)row * G + 4 * set;  // (4-aligned: G % 4 == 0)
+                const uint2 sv = *reinterpret_cast<const uint2 *>(scales + idx);
+                sw[j][v][0] = sv.x;
+                sw[j][v][1] = sv.y;
+                if constexpr (ASYM) {
+                    const uint2 zv = *reinterpret_cast<const uint2 *>(zeros + idx);
+                    zw[j][v][0] = zv.x;
+                    zw[j][v][1] = zv.y;
+                }
+            } else {
+                uint32_t h[4], hz[4];
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi) {
+                    const int64_t idx = (int64_t)row * G + min(4 * set + gi, G - 1);
+                    h[gi] = scales[idx];
+                    if constexpr (ASYM) hz[gi] = zeros[idx];
+                }
+                sw[j][v][0] = h[0] | (h[1] << 16);
+                sw[j][v][1] = h[2] | (h[3] << 16);
+                if constexpr (ASYM) {
+                    zw[j][v][0] = hz[0] | (hz[1] << 16);
+                    zw[j][v][1] = hz[2] | (hz[3] << 16);
+                }
+            }
+        }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int g = min(4 * set + gi, G - 1);
+            const uint8_t *base = planes + (((int64_t)tile * G + g) * 16 + c) * 16 + 4 * d;
+#pragma unroll
+            for (int p = 0; p < R; ++p)
+                pl[j][gi][p] = __builtin_nontemporal_load(
+                    reinterpret_cast<const uint32_t *>(base + p * plane_bytes));
+        }
+    };
+
+    // Activation operands of the current set: XB[gi][4j+e] is the bf16 pair of
+    // columns 128g + 32d + 8j + 2e (+1) of batch row bcol; the chains'
+    // starting values (corrections) and the group sums of X.
+    uint32_t XB[4][16];
+    float init[4], xsum[4];
+    auto load_set = [&](int set) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const int g = 4 * set + gi;
             const bool ok = bvalid && g < G;
             const int gc = g < G ? g : G - 1;
-            const u32x4_t *src =
-                reinterpret_cast<const u32x4_t *>(x + bclamp * ldx + 128 * gc + 32 * d);
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + bclamp * ldx + 128 * gc + 32 * d);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4_t v = ok ? src[j] : u32x4_t{0u, 0u, 0u, 0u};
-                XB[gi][4 * j] = v.x; XB[gi][4 * j + 1] = v.y;
-                XB[gi][4 * j + 2] = v.z; XB[gi][4 * j + 3] = v.w;
+                XB[gi][4 * j] = v.x;
+                XB[gi][4 * j + 1] = v.y;
+                XB[gi][4 * j + 2] = v.z;
+                XB[gi][4 * j + 3] = v.w;
             }
+        }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
             float corr = correction<R, 16>(XB[gi]);
             corr += __shfl_xor(corr, 16);
             corr += __shfl_xor(corr, 32);
-            init[gi] = f32x4_t{corr, corr, corr, corr};
-            xsum[gi] = 0.f;
-            if (zeros) {
+            init[gi] = corr;
+            if constexpr (ASYM) {
                 const uint32_t one = 0x3F803F80u;
                 float sx = 0.f;
 #pragma unroll
                 for (int m = 0; m < 16; ++m)
                     sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
-                                                         __builtin_bit_cast(bf16x2_t, XB[gi][m]),
-                                                         sx, false);
+                                                         __builtin_bit_cast(bf16x2_t, XB[gi][m]), sx,
+                                                         false);
                 sx += __shfl_xor(sx, 16);
                 sx += __shfl_xor(sx, 32);
                 xsum[gi] = sx;
             }
         }
+    };
 
-        // Plane words: lane (c, d) reads word d of row c's chunk, per plane.
-        uint32_t pl[TM][4][R];
+    auto compute = [&](int j) {
+        f32x4_t out = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            const int tile = min(tile0 + t, tiles_total - 1);
+        for (int gi = 0; gi < 4; ++gi) {
+            uint32_t D0[16], D1[16];
+            decode_word<R>(pl[j][gi], D0, D1);
+            f32x4_t P = {init[gi], init[gi], init[gi], init[gi]};
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                const int g = 4 * set + gi;
-                const int gc = g < G ? g : G - 1;
-                const uint8_t *base = planes + (((int64_t)tile * G + gc) * 16 + c) * 16 + 4 * d;
-#pragma unroll
-                for (int p = 0; p < R; ++p)
-                    pl[t][gi][p] = __builtin_nontemporal_load(
-                        reinterpret_cast<const uint32_t *>(base + p * plane_bytes));
-            }
-        }
-
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-#pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                const int g = 4 * set + gi;
-                uint32_t D0[16], D1[16];
-                decode_word<R>(pl[t][gi], D0, D1);
-                f32x4_t P = init[gi];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32x4_t xb = {XB[gi][4 * j], XB[gi][4 * j + 1], XB[gi][4 * j + 2],
-                                        XB[gi][4 * j + 3]};
-                    const u32x4_t a0 = {D0[4 * j], D0[4 * j + 1], D0[4 * j + 2], D0[4 * j + 3]};
-                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                                __builtin_bit_cast(bf16x8_t, xb), P,
-                                                                0, 0, 0);
-                    if constexpr (Phases<R>::count == 2) {
-                        const u32x4_t a1 = {D1[4 * j], D1[4 * j + 1], D1[4 * j + 2],
-                                            D1[4 * j + 3]};
-                        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, xb), P,
-                            0, 0, 0);
-                    }
-                }
-                // Output layout: this lane holds rows 4d..4d+3 of the tile, batch bcol.
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 16 * (tile0 + t) + 4 * d + v;
-                    float s = 0.f, pv = P[v];
-                    if (g < G && t < tcount && row < n) {
-                        s = sb_bf16_to_f32(scales[(int64_t)row * G + g]);
-                        if (zeros) {  // + (127.5 - z) * 2^(R-8) * group sum of X
-                            const float z = sb_bf16_to_f32(zeros[(int64_t)row * G + g]);
-                            pv = fmaf((127.5f - z) * (1.0f / (float)(1 << (8 - R))), xsum[gi], pv);
-                        }
-                    }
-                    acc[t][v] = fmaf(s, pv, acc[t][v]);
+            for (int jj = 0; jj < 4; ++jj) {
+                const u32x4_t xb = {XB[gi][4 * jj], XB[gi][4 * jj + 1], XB[gi][4 * jj + 2], XB[gi][4 * jj + 3]};
+                const u32x4_t a0 = {D0[4 * jj], D0[4 * jj + 1], D0[4 * jj + 2], D0[4 * jj + 3]};
+                P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
+                                                            __builtin_bit_cast(bf16x8_t, xb), P, 0, 0, 0);
+                if constexpr (NPH == 2) {
+                    const u32x4_t a1 = {D1[4 * jj], D1[4 * jj + 1], D1[4 * jj + 2], D1[4 * jj + 3]};
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1),
+                                                                __builtin_bit_cast(bf16x8_t, xb), P, 0, 0, 0);
                 }
             }
+            // This lane holds rows 4d..4d+3 of the tile for batch row bcol.
+            // (No guard on the scale: a group past k has zero activations, so
+            // its chain is zero, and rows past n are never stored.)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t word = sw[j][v][gi >> 1];
+                const float s = sb_bf16_to_f32((gi & 1) ? (word >> 16) : (word & 0xFFFFu));
+                float pv = P[v];
+                if constexpr (ASYM) {  // + (127.5 - z) * 2^(R-8) * sum of the group's X
+                    const uint32_t zword = zw[j][v][gi >> 1];
+                    const float z = sb_bf16_to_f32((gi & 1) ? (zword >> 16) : (zword & 0xFFFFu));
+                    pv = fmaf((127.5f - z) * (1.0f / (float)(1 << (8 - R))), xsum[gi], pv);
+                }
+                out[v] = fmaf(s, pv, out[v]);
+            }
         }
+        return out;
+    };
+    // Add a tile's four outputs to this lane's slot: an add that returns
+    // nothing, so the wave does not wait for it; one writer per slot, so the
+    // order of the additions is fixed.
+    auto commit = [&](int t, const f32x4_t &v4) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            __hip_atomic_fetch_add(&slot[(t * 4 + v) * 64 + lane], v4[v], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+
+    for (int si = 0; si < my_sets; ++si) {
+        const int set = w + si * W;
+        // The set's activations first (staging them waits for nothing else:
+        // a set starts with no loads in flight), then the first PD tiles.
+        load_set(set);
+#pragma unroll
+        for (int j = 0; j < PD; ++j) {
+            // (in order: the loads in flight at the loop top then match the
+            // steady state, and the waits there stay partial)
+            __builtin_amdgcn_sched_barrier(0);
+            load_step(j, set, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int Tfull = T / PD * PD;
+        for (int t0 = 0; t0 < Tfull; t0 += PD) {
+#pragma unroll
+            for (int j = 0; j < PD; ++j) {
+                const f32x4_t v4 = compute(j);
+                load_step(j, set, t0 + j + PD);  // refill as soon as the buffer is free
+                commit(t0 + j, v4);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < PD; ++j)  // the last < PD tiles are already loaded
+            if (Tfull + j < T) commit(Tfull + j, compute(j));
     }
 
-#pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[w][t][v][lane] = acc[t][v];
+    // Outputs: add the waves' slots in a fixed order.
     __syncthreads();
     const float post = (float)(1 << (8 - R));
-    for (int e = threadIdx.x; e < TM * 4 * 64; e += blockDim.x) {
-        const int t = e / 256, v = (e / 64) & 3, l = e & 63;
+    for (int e = threadIdx.x; e < T * 256; e += blockDim.x) {
+        const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
         float sum = 0.f;
-        for (int ww = 0; ww < W; ++ww) sum += red[ww][t][v][l];
-        const int row = 16 * (tile0 + t) + 4 * (l >> 4) + v;
+        for (int ww = 0; ww < W; ++ww) sum += red[((size_t)ww * tiles_per_wg + t) * 256 + v * 64 + l];
+        const int row = 16 * (t_begin + t) + 4 * (l >> 4) + v;
         const int64_t b = (int64_t)blockIdx.y * 16 + (l & 15);
-        if (t < tcount && row < n && b < batch) store_y(y, ybf16, b * ldy + row, sum * post);
+        if (row < n && b < batch) store_y(y, ybf16, b * ldy + row, sum * post);
     }
 }
 
-template <int R, int TM>
-static void launch_tm(const QgemmArgs &a, int waves, hipStream_t stream) {
+// About one workgroup per CU, each owning a run of 16-row tiles.
+static int smallb_tpw(const QgemmArgs &a, int cu_count) {
     const int tiles = (a.n + 15) / 16;
-    dim3 grid((unsigned)((tiles + TM - 1) / TM), (unsigned)((a.batch + 15) / 16));
-    hipLaunchKernelGGL((smallb_kernel<R, TM>), grid, dim3(64 * waves), 0, stream, a.x, a.batch,
-                       a.ldx, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, a.y,
-                       a.ldy, a.ybf16);
+    int tpw = (tiles + cu_count / 2) / cu_count;
+    if (tpw > SMALLB_MAX_TILES) tpw = SMALLB_MAX_TILES;
+    if (tpw < 1) tpw = 1;
+    return tpw;
 }
 
-static int smallb_tm(const QgemmArgs &a, int cu_count) {
+template <int R, bool ASYM, bool S4>
+static void launch_v(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int tiles = (a.n + 15) / 16;
-    return tiles >= 4 * cu_count ? 2 : 1;
+    const int tpw = smallb_tpw(a, cu_count);
+    dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)((a.batch + 15) / 16));
+    hipLaunchKernelGGL((smallb_kernel<R, SMALLB_DEPTH, ASYM, S4>), grid, dim3(64 * SMALLB_WAVES),
+                       smallb_lds_bytes(SMALLB_WAVES, tpw), stream, a.x, a.batch, a.ldx, a.planes,
+                       a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, tpw, a.y, a.ldy, a.ybf16);
 }
 
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
-    const int G = a.k / 128;
-    const int nsets = (G + 3) / 4;
-    const int waves = nsets < SMALLB_MAX_WAVES ? nsets : SMALLB_MAX_WAVES;
-    if (smallb_tm(a, cu_count) == 2) launch_tm<R, 2>(a, waves, stream);
-    else launch_tm<R, 1>(a, waves, stream);
+    const bool s4 = ((a.k / 128) & 3) == 0;
+    if (a.zeros) {
+        if (s4) launch_v<R, true, true>(a, cu_count, stream);
+        else launch_v<R, true, false>(a, cu_count, stream);
+    } else {
+        if (s4) launch_v<R, false, true>(a, cu_count, stream);
+        else launch_v<R, false, false>(a, cu_count, stream);
+    }
 }
 
 void smallb_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
-    snprintf(out, len, "nbw::smallb_kernel<%d, %d>", r, smallb_tm(a, cu_count));
+    (void)cu_count;
+    snprintf(out, len, "nbw::smallb_kernel<%d, %d, %s, %s>", r, SMALLB_DEPTH, a.zeros ? "true" : "false",
+             ((a.k / 128) & 3) == 0 ? "true" : "false");
 }
 
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {
