@@ -19,7 +19,10 @@ copy from a rotation of copies totalling >1.2 GB.
 
 Extra fields: per-kernel durations (each product replayed back to back in a
 graph over the copy rotation, HIP events around the replays) giving the
-dominant kernel's roofline; the 12 products as 3 grouped dispatches; batch 4
+dominant kernel's roofline, and beside each product the time a plain streaming
+read of the same plane bytes takes in one launch (nbw_stream_read, same rotation
+and timing: the floor a launch of that size cannot beat, well under the 8 TB/s
+peak for tens of MB); the 12 products as 3 grouped dispatches; batch 4
 and 16 on the same linears; batch 256 (TFLOP/s, r in 8, 4, 3, 2, activations
 with 1% outlier channels x10); the CPU oracle timed on this host on a bounded
 sample of the batch-1 step.
@@ -181,6 +184,27 @@ def kernel_durations(torch, nbw, layer, rs, xkey, ykey, batch, kernel, reps):
             ms = event_time(torch, lambda i: g.replay(), reps)
             out[(L["name"], r)] = {"us": ms * 1e3 / len(calls), "n": L["n"], "k": L["k"],
                                    "kernel": nbw.kernel_name(batch, L["n"], L["k"], r, kernel)}
+            del g
+    return out
+
+
+def stream_floor(torch, nbw, layer, rs, reps):
+    """Back-to-back duration of a plain streaming read of each product's plane bytes.
+
+    The same rotation and timing as kernel_durations, with the library's
+    streaming-read reference (nbw_stream_read) in place of the product: the
+    time one launch needs to read those bytes and do nothing else.  Returns
+    {(linear, r): us per launch}."""
+    sink = nbw.stream_sink()
+    out = {}
+    for r in rs:
+        for L in layer.lin:
+            nbytes = r * L["w"][0].plane_bytes
+            bufs = [L["w"][c].storage for c in range(layer.copies)]
+            g = capture(torch, lambda bl=bufs, nb=nbytes: [nbw.stream_read(b, nb, sink) for b in bl])
+            g.replay()
+            ms = event_time(torch, lambda i: g.replay(), reps)
+            out[(L["name"], r)] = ms * 1e3 / len(bufs)
             del g
     return out
 
@@ -365,13 +389,21 @@ def main():
                 "kernel": dom_name, "avg_launch_us": round(dom_avg_us, 2),
                 "bytes_per_launch": dom["bytes"] // dom["launches"],
                 "launches_per_step": dom["launches"]}
+    floor = stream_floor(torch, nbw, layer, RS_B1, reps=max(10, args.steps // 4))
     per_shape = [{"linear": nm, "r": r, "us": round(d["us"], 2),
                   "GBps": round(r * d["n"] * d["k"] / 8 / (d["us"] * 1e-6) / 1e9, 1),
+                  "read_floor_us": round(floor[(nm, r)], 2),
+                  "frac_of_read_floor": round(floor[(nm, r)] / d["us"], 3),
                   "kernel": d["kernel"]}
                  for (nm, r), d in sorted(durs.items())]
-    log(f"dominant kernel {dom_name}: {dom_avg_us:.2f} us avg, {achieved:.1f} GB/s")
+    dom_floor = sum(floor[key] for key, d in durs.items() if d["kernel"] == dom_name)
+    roofline["read_floor_us_per_launch"] = round(dom_floor / dom["launches"], 2)
+    roofline["frac_of_read_floor"] = round(dom_floor / dom["us"], 3)
+    log(f"dominant kernel {dom_name}: {dom_avg_us:.2f} us avg, {achieved:.1f} GB/s; "
+        f"a plain read of the same bytes takes {dom_floor / dom['launches']:.2f} us")
     for p in per_shape:
-        log(f"  {p['linear']:8s} r={p['r']} {p['us']:7.2f} us {p['GBps']:7.1f} GB/s  {p['kernel']}")
+        log(f"  {p['linear']:8s} r={p['r']} {p['us']:7.2f} us {p['GBps']:7.1f} GB/s  "
+            f"(read floor {p['read_floor_us']:6.2f} us, {p['frac_of_read_floor']:.2f})  {p['kernel']}")
 
     result = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),

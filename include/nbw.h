@@ -206,6 +206,22 @@ nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *s
  * uint8 [n][k].  A test hook for the bit-exact slicing check. */
 nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, void *stream);
 
+/* Bandwidth reference for the batch-1 products (MatGPTQ: Efficient and
+ * Accurate Inference over Nested Quantized Models, Table 1: an r-bit child
+ * loads r/8 bytes per weight, so a batch-1 product is a single pass over its
+ * plane bytes): one launch that reads the device range [src, src + bytes)
+ * with 16-byte loads and does nothing else, i.e. the time floor a product
+ * of that many plane bytes is measured against.
+ * src: device pointer, 16-byte aligned; bytes: a multiple of 16, >= 0.
+ * sink: device uint32 array of nbw_stream_sink_words() words (caller-owned),
+ * fully written: word i is the XOR of the 32-bit words wave i read, so the
+ * XOR of all sink words is the XOR of every 32-bit word of the range.
+ * Errors: NBW_EINVAL (null pointer, negative or non-multiple-of-16 bytes),
+ * NBW_EALIGN (src or sink misaligned), NBW_EHIP (launch failed).  Asynchronous
+ * on `stream`. */
+int32_t nbw_stream_sink_words(void);
+nbw_status nbw_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
 /* Name of the kernel template instance nbw_qgemm_kernel would launch for
  * this problem on the current device (for example "nbw::gemv_kernel<4, 1, 2>",
  * as profilers print it without the parameter list), or "" on bad input.  The

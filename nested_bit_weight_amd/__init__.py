@@ -61,7 +61,7 @@ _LIB = None
 
 EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
            "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex", "nbw_qgemm_grouped",
-           "nbw_choose_codes", "nbw_unpack_codes",
+           "nbw_choose_codes", "nbw_unpack_codes", "nbw_stream_sink_words", "nbw_stream_read",
            "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
 
 
@@ -96,6 +96,10 @@ def _lib():
         lib.nbw_qgemm_grouped.restype = ctypes.c_int
         lib.nbw_unpack_codes.argtypes = [pv, i32, vp, vp]
         lib.nbw_unpack_codes.restype = ctypes.c_int
+        lib.nbw_stream_sink_words.argtypes = []
+        lib.nbw_stream_sink_words.restype = i32
+        lib.nbw_stream_read.argtypes = [vp, i64, vp, vp]
+        lib.nbw_stream_read.restype = ctypes.c_int
         lib.nbw_status_str.argtypes = [ctypes.c_int]
         lib.nbw_status_str.restype = ctypes.c_char_p
         lib.nbw_last_hip_error.argtypes = []
@@ -375,6 +379,22 @@ def unpack_codes(w: PackedWeight, r: int) -> torch.Tensor:
     return out
 
 
+def stream_sink(device=None) -> torch.Tensor:
+    """A sink buffer for stream_read (nbw_stream_sink_words() uint32 words)."""
+    return torch.empty(_lib().nbw_stream_sink_words(), dtype=torch.int32,
+                       device=device if device is not None else "cuda")
+
+
+def stream_read(src: torch.Tensor, nbytes: int, sink: torch.Tensor) -> None:
+    """Launch the plain streaming read of the first nbytes of src (bandwidth reference)."""
+    if sink.numel() < _lib().nbw_stream_sink_words() or sink.dtype != torch.int32:
+        raise ValueError(f"stream_read: sink needs {_lib().nbw_stream_sink_words()} int32 words")
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("stream_read: nbytes exceeds the source tensor")
+    _check(_lib().nbw_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes,
+                                  ctypes.c_void_p(sink.data_ptr()), _stream(src)), "nbw_stream_read")
+
+
 def kernel_name(batch: int, n: int, k: int, r: int, kernel: str = "auto") -> str:
     """Name of the kernel instance nbw_qgemm would launch (as profilers print it)."""
     return _lib().nbw_kernel_name(batch, n, k, r, KERNELS[kernel]).decode()
@@ -384,6 +404,6 @@ def version() -> str:
     return _lib().nbw_version().decode()
 
 
-__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "choose_codes", "unpack_codes", "plane_bytes",
+__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]

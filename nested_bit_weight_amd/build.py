@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnbw.so")
-SOURCES = ["abi.hip", "pack.hip", "gemv.hip", "smallb.hip", "gemm.hip", "choose.hip"]
+SOURCES = ["abi.hip", "pack.hip", "gemv.hip", "smallb.hip", "gemm.hip", "choose.hip", "stream.hip"]
 ARCH = "gfx950"
 
 

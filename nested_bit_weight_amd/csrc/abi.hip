@@ -250,6 +250,15 @@ nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, v
     return e == hipSuccess ? NBW_OK : hip_failed(e);
 }
 
+int32_t nbw_stream_sink_words(void) { return nbw::stream_sink_words(); }
+
+nbw_status nbw_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
+    if (!src || !sink || bytes < 0 || bytes % 16) return NBW_EINVAL;
+    if (!aligned(src, 16) || !aligned(sink, 4)) return NBW_EALIGN;
+    hipError_t e = nbw::launch_stream_read(src, bytes, sink, (hipStream_t)stream);
+    return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
 const char *nbw_kernel_name(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_kernel kernel) {
     thread_local char buf[96];
     if (!shape_ok(n, k) || batch < 1 || r < 1 || r > 8 || kernel < NBW_KERNEL_AUTO ||

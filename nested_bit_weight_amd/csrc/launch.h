@@ -50,6 +50,11 @@ hipError_t launch_gemv(int r, const QgemmArgs &a, int cu_count, hipStream_t stre
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 
+// Plain streaming read of [src, src + bytes) (bytes a multiple of 16), one
+// XOR word per wave into sink (stream_sink_words() words).
+int stream_sink_words();
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+
 // Grouped batch-1 launch: several products (each with its own r) as one
 // dispatch.  Eligible problems: batch 1, shapes the streaming kernel takes.
 int gemv_group_capacity();

@@ -174,3 +174,14 @@ def test_choose_codes_validation(lib):
     assert call([8], [1.0], k=100) == EINVAL
     assert call([8], [1.0], w=0) == EINVAL
     assert call([8], [1.0], w=FAKE + 2) == EALIGN
+
+
+def test_stream_read_validation(lib):
+    vp = ctypes.c_void_p
+    assert lib.nbw_stream_sink_words() >= 1024
+    assert lib.nbw_stream_read(None, 1024, vp(FAKE), None) == EINVAL
+    assert lib.nbw_stream_read(vp(FAKE), 1024, None, None) == EINVAL
+    assert lib.nbw_stream_read(vp(FAKE), -16, vp(FAKE), None) == EINVAL
+    assert lib.nbw_stream_read(vp(FAKE), 1000, vp(FAKE), None) == EINVAL   # not a multiple of 16
+    assert lib.nbw_stream_read(vp(FAKE + 8), 1024, vp(FAKE), None) == EALIGN
+    assert lib.nbw_stream_read(vp(FAKE), 1024, vp(FAKE + 2), None) == EALIGN
