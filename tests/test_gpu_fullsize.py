@@ -1,0 +1,98 @@
+"""GPU parity at the workloads' full sizes, beyond the Llama-3.1-8B layer.
+
+* the single 1024 x 1024 linear (uniform parent codes, scales U(0.001, 0.01),
+  X ~ N(0, 1), batch 1, r = 8, 4, 2): every output against the fp64 oracle,
+  on every kernel;
+* the Qwen3-8B-shaped linears (batch 1, 4, 32, 256; r = 6, 4, 3, 2) and the
+  70B-shaped layer (batch 1, 16, 128; r = 3, 2) at full size, through the
+  automatic kernel choice (the launch configuration the bench times): the
+  output rows of the first and last tiles plus 59 seeded rows against the
+  oracle, which packs those rows' codes itself.
+
+Bars as in test_gpu_parity: max |Y - R| / max |R| per batch row <= 2e-3 (the
+contract) and <= 1e-4 (exact bf16 operands, fp32 accumulation).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT = 2e-3
+DESIGN_BOUND = 1e-4
+
+
+@pytest.fixture(scope="module")
+def nbw():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nested_bit_weight_amd as m
+    m.library()
+    return m
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t.view(dtype) if dtype is not None else t).cuda()
+
+
+def rel_err(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    return float((np.abs(y - ref).max(axis=1) / den).max())
+
+
+@pytest.mark.parametrize("kernel", ["gemv", "smallb", "gemm"])
+def test_single_1024_every_output(nbw, kernel):
+    d = synth.make_linear("single-1024", 0, 1)
+    n, k = d["n"], d["k"]
+    planes = oracle.pack(d["codes"])
+    w = nbw.pack_bitplanes(dev(d["codes"]))
+    x = dev(d["x"], torch.bfloat16)
+    s = dev(d["scales"], torch.bfloat16)
+    for r in (8, 4, 2):
+        y = nbw.qgemm(x, nbw.slice_view(w, r), s, r, kernel=kernel).cpu().numpy()
+        e = rel_err(y, oracle.qgemm(d["x"], planes, d["scales"], n, k, r))
+        print(f"single-1024 {kernel} r={r} err={e:.3e}", flush=True)
+        assert e <= CONTRACT and e <= DESIGN_BOUND
+
+
+@functools.lru_cache(maxsize=1)
+def _layer(workload, shape_id, batch):
+    return synth.make_linear(workload, shape_id, batch)
+
+
+def _sampled(nbw, workload, shape_id, batches, rs):
+    d = _layer(workload, shape_id, max(batches))
+    n, k = d["n"], d["k"]
+    rng = np.random.default_rng(1000 + shape_id)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n), rng.integers(0, n, 59)]))
+    sub_planes = oracle.pack(np.ascontiguousarray(d["codes"][rows]))
+    sub_scales = np.ascontiguousarray(d["scales"][rows])
+    w = nbw.pack_bitplanes(dev(d["codes"]))
+    s = dev(d["scales"], torch.bfloat16)
+    for b in batches:
+        xb = np.ascontiguousarray(d["x"][:b])
+        x = dev(xb, torch.bfloat16)
+        for r in rs:
+            print(f"{workload} {d['name']} b={b} r={r} kernel={nbw.kernel_name(b, n, k, r)}", flush=True)
+            y = nbw.qgemm(x, nbw.slice_view(w, r), s, r).cpu().numpy()
+            assert np.all(np.isfinite(y))
+            ref = oracle.qgemm(xb, sub_planes, sub_scales, len(rows), k, r)
+            e = rel_err(y[:, rows], ref)
+            print(f"  err={e:.3e}", flush=True)
+            assert e <= CONTRACT and e <= DESIGN_BOUND
+
+
+@pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
+def test_qwen3_8b_full_size_sampled(nbw, shape_id):
+    _sampled(nbw, "qwen3-8b", shape_id, (1, 4, 32, 256), (6, 4, 3, 2))
+
+
+@pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
+def test_llama70b_full_size_sampled(nbw, shape_id):
+    _sampled(nbw, "llama-70b", shape_id, (1, 16, 128), (3, 2))
