@@ -208,12 +208,17 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         }
         return s * (P + cg);
     };
-    // Accumulate into this lane's own LDS slot for the tile: an add that
-    // returns nothing, so the wave does not wait for it.  Each slot has a
-    // single writer, so the order of the additions is fixed.
+    // Accumulate into this lane's own LDS slot for the tile.  Each slot has a
+    // single writer (this lane), so no atomic is needed and the order of the
+    // additions is fixed: the wave's first set stores, later sets read, add
+    // and store.  (LDS float atomics serialize across the CU: one wave-wide
+    // ds_add_f32 per step cost about a microsecond per launch.)
     auto commit = [&](float v) {
-        __hip_atomic_fetch_add(&red[(w * slots + ct) * 64 + lane], v,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        float *slot = &red[(w * slots + ct) * 64 + lane];
+        if (cs == 0)
+            *slot = v;
+        else
+            *slot += v;
         if (++ct == T) {
             ct = 0;
             ++cs;
