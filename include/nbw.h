@@ -153,14 +153,34 @@ typedef struct nbw_qgemm_opts {
                            (the pages evaluate an asymmetric variant, MatGPTQ v2
                            Tables 4-7, without stating its formula; z = 127.5
                            gives the symmetric child exactly). */
+    void *workspace;    /* NULL, or caller-owned device scratch (256-byte
+                           aligned) of workspace_bytes bytes; no initial
+                           contents are needed.  When it holds at least
+                           nbw_qgemm_workspace_bytes(...) bytes, a large-batch
+                           launch that splits k meets its splits there: each
+                           split stores its fp32 partial tile and a second
+                           launch on the same stream adds them in a fixed order
+                           (deterministic, fp32 or bf16 Y).  Without it such a
+                           launch clears Y and adds fp32 partial sums with
+                           atomics (fp32 Y only; bf16 Y then runs unsplit).
+                           Calls that overlap in time must not share a
+                           workspace. */
+    int64_t workspace_bytes;
 } nbw_qgemm_opts;
 
-/* nbw_qgemm with row strides, a bf16 output and asymmetric children
- * (opts == NULL: as nbw_qgemm).  y points at fp32 or bf16 elements per
- * opts->y_dtype; only the first n elements of each Y row are written.  Same
- * errors as nbw_qgemm, plus NBW_EINVAL for a stride below k or n and
- * NBW_EALIGN for a stride that breaks the row alignment; NBW_EUNSUPPORTED
- * for an unknown y_dtype or kernel. */
+/* Bytes of workspace nbw_qgemm_ex uses for this problem and kernel choice
+ * (0: the launch does not split k, or batch is 0, and needs none), or -1 on
+ * bad arguments.
+ * Host only; queries the device's compute-unit count once. */
+int64_t nbw_qgemm_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_kernel kernel);
+
+/* nbw_qgemm with row strides, a bf16 output, asymmetric children and a
+ * split-k workspace (opts == NULL: as nbw_qgemm).  y points at fp32 or bf16
+ * elements per opts->y_dtype; only the first n elements of each Y row are
+ * written.  Same errors as nbw_qgemm, plus NBW_EINVAL for a stride below k or
+ * n or a negative workspace_bytes, NBW_EALIGN for a stride that breaks the row
+ * alignment or a misaligned workspace; NBW_EUNSUPPORTED for an unknown
+ * y_dtype or kernel. */
 nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
                         const void *scales_bf16, int32_t r, void *y, const nbw_qgemm_opts *opts,
                         void *stream);

@@ -46,7 +46,8 @@ class WView(ctypes.Structure):
 
 class QgemmOpts(ctypes.Structure):
     _fields_ = [("ldx", ctypes.c_int64), ("ldy", ctypes.c_int64), ("y_dtype", ctypes.c_int32),
-                ("kernel", ctypes.c_int32), ("zeros_bf16", ctypes.c_void_p)]
+                ("kernel", ctypes.c_int32), ("zeros_bf16", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
 Y_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -60,7 +61,8 @@ class Problem(ctypes.Structure):
 _LIB = None
 
 EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
-           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex", "nbw_qgemm_grouped",
+           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex",
+           "nbw_qgemm_workspace_bytes", "nbw_qgemm_grouped",
            "nbw_choose_codes", "nbw_unpack_codes", "nbw_stream_sink_words", "nbw_stream_read",
            "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
 
@@ -96,6 +98,8 @@ def _lib():
         lib.nbw_qgemm_grouped.restype = ctypes.c_int
         lib.nbw_unpack_codes.argtypes = [pv, i32, vp, vp]
         lib.nbw_unpack_codes.restype = ctypes.c_int
+        lib.nbw_qgemm_workspace_bytes.argtypes = [i64, i64, i64, i32, ctypes.c_int]
+        lib.nbw_qgemm_workspace_bytes.restype = i64
         lib.nbw_stream_sink_words.argtypes = []
         lib.nbw_stream_sink_words.restype = i32
         lib.nbw_stream_read.argtypes = [vp, i64, vp, vp]
@@ -231,12 +235,14 @@ def _need_rows(t: torch.Tensor, name: str, dtype, cols: int) -> None:
 
 def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
           out: torch.Tensor | None = None, kernel: str = "auto", zeros: torch.Tensor | None = None,
-          out_dtype=torch.float32) -> torch.Tensor:
+          out_dtype=torch.float32, workspace="auto") -> torch.Tensor:
     """Y [B][n] = X . dequant_r(W)^T for the r-bit child of ``w``.
 
     ``x`` may have a row stride larger than k (e.g. a column slice of a wider
     tensor), as may ``out``; ``zeros`` (bf16 [n][k/128]) selects asymmetric
-    children; ``out_dtype`` is torch.float32 or torch.bfloat16."""
+    children; ``out_dtype`` is torch.float32 or torch.bfloat16.  ``workspace``:
+    "auto" (the binding's buffer for this device and stream), a uint8 device
+    tensor, or None (split k through fp32 atomics)."""
     _need(scales, "scales", torch.bfloat16, 2)
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-d tensor")
@@ -260,9 +266,18 @@ def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
         _need_rows(out, "out", out_dtype, w.n)
         if out.shape[0] != b or out.device != x.device:
             raise ValueError(f"out must be [{b}][{w.n}] on the same GPU")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', a tensor or None")
+        dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+        workspace = _workspace(dev, _raw_stream(dev), workspace_bytes(b, w.n, w.k, r, kernel))
+    if workspace is not None and (workspace.device != x.device or workspace.dtype != torch.uint8):
+        raise ValueError("workspace must be a uint8 tensor on the inputs' GPU")
     opts = QgemmOpts(x.stride(0) if b > 1 else k, out.stride(0) if b > 1 else w.n,
                      Y_DTYPES[out_dtype], KERNELS[kernel],
-                     zeros.data_ptr() if zeros is not None else None)
+                     zeros.data_ptr() if zeros is not None else None,
+                     workspace.data_ptr() if workspace is not None else None,
+                     workspace.numel() if workspace is not None else 0)
     _check(_lib().nbw_qgemm_ex(ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(w.view),
                                ctypes.c_void_p(scales.data_ptr()), r,
                                ctypes.c_void_p(out.data_ptr()), ctypes.byref(opts), _stream(x)),
@@ -292,6 +307,30 @@ def choose_codes(w: torch.Tensor, scales: torch.Tensor, widths=(3, 4, 8),
     return out
 
 
+_WORKSPACES = {}
+
+
+def workspace_bytes(batch: int, n: int, k: int, r: int, kernel: str = "auto") -> int:
+    """Bytes of split-k workspace nbw_qgemm_ex uses for this problem (0: none)."""
+    nb = _lib().nbw_qgemm_workspace_bytes(batch, n, k, r, KERNELS[kernel])
+    if nb < 0:
+        raise ValueError("workspace_bytes: bad arguments")
+    return nb
+
+
+def _workspace(device_index: int, stream: int, nbytes: int):
+    """The binding's split-k workspace for (device, stream): calls on one
+    stream never overlap, so one buffer per stream suffices."""
+    if nbytes <= 0:
+        return None
+    key = (device_index, stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device("cuda", device_index))
+        _WORKSPACES[key] = ws
+    return ws
+
+
 class QgemmCall:
     """One qgemm with its arguments checked and marshalled once.
 
@@ -300,7 +339,7 @@ class QgemmCall:
     kept alive by the object.  Use it where per-call Python cost matters, e.g. when a
     decode step is captured into a HIP graph or launched in a tight loop."""
 
-    __slots__ = ("x", "w", "scales", "r", "out", "kernel", "_args", "_fn", "_dev")
+    __slots__ = ("x", "w", "scales", "r", "out", "kernel", "_args", "_fn", "_dev", "_ws", "_opts")
 
     def __init__(self, x, w, scales, r, out=None, kernel="auto"):
         _need(x, "x", torch.bfloat16, 2)
@@ -321,12 +360,17 @@ class QgemmCall:
         if kernel not in KERNELS:
             raise ValueError(f"unknown kernel {kernel!r}")
         self.x, self.w, self.scales, self.r, self.out, self.kernel = x, w, scales, r, out, kernel
+        self._dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+        nb = workspace_bytes(b, w.n, w.k, r, kernel)
+        self._ws = _workspace(self._dev, _raw_stream(self._dev), nb)
+        self._opts = QgemmOpts(0, 0, 0, KERNELS[kernel], None,
+                               self._ws.data_ptr() if self._ws is not None else None,
+                               self._ws.numel() if self._ws is not None else 0)
         view = WView.from_buffer_copy(w.view)  # byref() below keeps it alive
         self._args = (ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(view),
                       ctypes.c_void_p(scales.data_ptr()), r, ctypes.c_void_p(out.data_ptr()),
-                      KERNELS[kernel])
-        self._fn = _lib().nbw_qgemm_kernel
-        self._dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+                      ctypes.byref(self._opts))
+        self._fn = _lib().nbw_qgemm_ex
 
     def __call__(self, stream=None):
         if stream is None:
@@ -404,6 +448,6 @@ def version() -> str:
     return _lib().nbw_version().decode()
 
 
-__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "plane_bytes",
+__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "workspace_bytes", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]

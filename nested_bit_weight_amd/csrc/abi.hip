@@ -125,6 +125,8 @@ nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
     if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scales_bf16, 4)) return NBW_EALIGN;
     if (o.zeros_bf16 && !aligned(o.zeros_bf16, 4)) return NBW_EALIGN;
     if (ldx % 8 != 0) return NBW_EALIGN;  // X rows are read with 16-byte loads
+    if (o.workspace_bytes < 0) return NBW_EINVAL;
+    if (o.workspace && !aligned(o.workspace, 256)) return NBW_EALIGN;
     int cus = 0;
     st = cu_count(&cus);
     if (st != NBW_OK) return st;
@@ -144,6 +146,8 @@ nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
     a.ldy = ldy;
     a.ybf16 = ybf16 ? 1 : 0;
     a.zeros = (const uint16_t *)o.zeros_bf16;
+    a.ws = o.workspace;
+    a.ws_bytes = o.workspace ? o.workspace_bytes : 0;
     hipError_t e;
     switch (kernel) {
     case NBW_KERNEL_GEMV: e = nbw::launch_gemv(r, a, cus, (hipStream_t)stream); break;
@@ -248,6 +252,23 @@ nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, v
     hipError_t e = nbw::launch_unpack(r, (const uint8_t *)w->planes, w->plane_bytes, (int)w->n,
                                       (int)w->k, codes_out, (hipStream_t)stream);
     return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+int64_t nbw_qgemm_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_kernel kernel) {
+    if (!shape_ok(n, k) || batch < 0 || r < 1 || r > 8 || kernel < NBW_KERNEL_AUTO ||
+        kernel > NBW_KERNEL_GEMM)
+        return -1;
+    if (batch == 0) return 0;
+    if (kernel == NBW_KERNEL_AUTO)
+        kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
+    if (kernel != NBW_KERNEL_GEMM) return 0;
+    int cus = 0;
+    if (cu_count(&cus) != NBW_OK) return -1;
+    nbw::QgemmArgs a = {};
+    a.batch = batch;
+    a.n = (int)n;
+    a.k = (int)k;
+    return nbw::gemm_workspace_bytes(a, cus);
 }
 
 int32_t nbw_stream_sink_words(void) { return nbw::stream_sink_words(); }

@@ -58,9 +58,42 @@ __device__ __forceinline__ f32x16_t gm_mfma(const u32x4_t &a, const u32x4_t &b, 
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
+constexpr int GEMM_TILE = GEMM_BM * GEMM_BN;  // fp32 values of one partial tile
+
+// Stores one 32 x 32 accumulator block: the lane of half h and weight row
+// nrow holds batch rows brow + 8(v/4) + 4h + v%4 (v = 0..15) of column nrow,
+// each scaled by post; added with fp32 atomics or stored (fp32 or bf16).
+__device__ __forceinline__ void gemm_store_block(const f32x16_t &a, int brow, int h, int nrow,
+                                                 int n, int batch, float post, float *y,
+                                                 int64_t ldy, int ybf16, int atomic) {
+    if (nrow >= n) return;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int b = brow + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (b >= batch) continue;
+        const int64_t idx = (int64_t)b * ldy + nrow;
+        const float val = a[v] * post;
+        if (atomic)
+            __hip_atomic_fetch_add(y + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            store_y(y, ybf16, idx, val);
+    }
+}
+
+// Offset (in floats) of thread tid's accumulators (bb, 4q .. 4q+3) within a
+// partial tile: slice bb*4+q holds one float4 per thread, in thread order,
+// so both the stores here and the reads of the reduction are contiguous
+// across a wave.
+__device__ __forceinline__ int gemm_part_offset(int bb, int q, int tid) {
+    return ((bb * 4 + q) * GEMM_THREADS + tid) * 4;
+}
+
 // grid: (ceil(n / 256), ceil(batch / 128), splits); block 512.  Groups
-// [z * gps, min(G, (z + 1) * gps)) of k.  With atomic != 0 the result is added
-// to y (fp32, which the launcher has cleared); otherwise it is stored.  ASYM:
+// [z * gps, min(G, (z + 1) * gps)) of k.  Split k (splits > 1) either adds
+// fp32 partial sums into y with atomics (atomic != 0; the launcher has
+// cleared y), or, with a workspace (part != null), stores each split's partial
+// tile there for gemm_reduce_kernel to add in a fixed order.  ASYM:
 // asymmetric children, zeros bf16 [n][k/128]: each weight gains
 // s * (127.5 - z) over the symmetric child, i.e. the product gains
 // s * (127.5 - z) * 2^(R-8) * (group sum of the batch row's X), added through
@@ -69,7 +102,8 @@ template <int R, bool ASYM>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int batch, const uint8_t *__restrict__ planes,
     int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    int n, int k, int gps, float *__restrict__ y, int64_t ldy, int ybf16, int atomic) {
+    int n, int k, int gps, float *__restrict__ y, int64_t ldy, int ybf16, int atomic,
+    float *__restrict__ part) {
     __shared__ __align__(16) uint16_t xs[2][GEMM_BM * GEMM_XSTRIDE];
     // corrections (and group sums of X) of the last four groups, per batch row:
     // while group g runs, the pair (g-2, g-1) is read and g+1 is staged
@@ -108,18 +142,18 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     };
     auto stage_x = [&](int buf, int slot) {
         const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
-        float part = 0.f;
+        float cpart = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             *reinterpret_cast<u32x4_t *>(&xs[buf][xr * GEMM_XSTRIDE + 32 * qq + 8 * c]) = xv[c];
-            part = fmaf(pair_coef<R>(4 * c + 0), gm_dot2(one, xv[c].x, 0.f), part);
-            part = fmaf(pair_coef<R>(4 * c + 1), gm_dot2(one, xv[c].y, 0.f), part);
-            part = fmaf(pair_coef<R>(4 * c + 2), gm_dot2(one, xv[c].z, 0.f), part);
-            part = fmaf(pair_coef<R>(4 * c + 3), gm_dot2(one, xv[c].w, 0.f), part);
+            cpart = fmaf(pair_coef<R>(4 * c + 0), gm_dot2(one, xv[c].x, 0.f), cpart);
+            cpart = fmaf(pair_coef<R>(4 * c + 1), gm_dot2(one, xv[c].y, 0.f), cpart);
+            cpart = fmaf(pair_coef<R>(4 * c + 2), gm_dot2(one, xv[c].z, 0.f), cpart);
+            cpart = fmaf(pair_coef<R>(4 * c + 3), gm_dot2(one, xv[c].w, 0.f), cpart);
         }
-        part += __shfl_xor(part, 1);
-        part += __shfl_xor(part, 2);
-        if (qq == 0) corr[slot][xr] = part;
+        cpart += __shfl_xor(cpart, 1);
+        cpart += __shfl_xor(cpart, 2);
+        if (qq == 0) corr[slot][xr] = cpart;
         if constexpr (ASYM) {
             float sx = 0.f;
 #pragma unroll
@@ -270,23 +304,62 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
             correct(h ? last : (last + 3) & 3, h ? s_prev : s_prev2, h ? zs_prev : zs_prev2);
     }
 
-    // Epilogue: lane holds rows b0 + 32bb + 8(v/4) + 4h + v%4 of column nrow.
-    if (nrow < n) {
-        const float post = (float)(1 << (8 - R));
+    // Split k through the workspace: store the raw partial tile and leave
+    // the sum and the output to gemm_reduce_kernel (a later launch, so no
+    // fence or counter is needed between the splits).
+    if (part) {
+        float *dst = part + ((size_t)blockIdx.z * gridDim.x * gridDim.y +
+                             blockIdx.y * gridDim.x + blockIdx.x) * GEMM_TILE;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int b = b0 + 32 * bb + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (b >= batch) continue;
-                const int64_t idx = (int64_t)b * ldy + nrow;
-                const float val = acc[bb][v] * post;
-                if (atomic)
-                    __hip_atomic_fetch_add(y + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else
-                    store_y(y, ybf16, idx, val);
-            }
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4 *>(dst + gemm_part_offset(bb, q, tid)) =
+                    make_float4(acc[bb][4 * q], acc[bb][4 * q + 1], acc[bb][4 * q + 2], acc[bb][4 * q + 3]);
+        return;
     }
+
+    // Epilogue: lane holds rows b0 + 32bb + 8(v/4) + 4h + v%4 of column nrow.
+    const float post = (float)(1 << (8 - R));
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+        gemm_store_block(acc[bb], b0 + 32 * bb, h, nrow, n, batch, post, y, ldy, ybf16, atomic);
+}
+
+// Adds the S partial tiles of a split launch in the order z = 0..S-1 and
+// stores y (deterministic: the same sum on every run, any output type).
+// grid: (ceil(n / 256), ceil(batch / 128), 8 waves x 4 batch blocks); block
+// 64: workgroup (x, y, 4w + bb) finishes accumulator block bb of wave w of
+// the GEMM workgroup (x, y), with the GEMM's lane-to-element mapping.
+__global__ __launch_bounds__(64) void gemm_reduce_kernel(const float *__restrict__ part, int S,
+                                                         int batch, int n, float post,
+                                                         float *__restrict__ y, int64_t ldy,
+                                                         int ybf16) {
+    const int lane = threadIdx.x;
+    const int w = blockIdx.z >> 2, bb = blockIdx.z & 3;
+    const int tid = w * 64 + lane;
+    const int ntiles = gridDim.x * gridDim.y;
+    const float *src = part + (size_t)(blockIdx.y * gridDim.x + blockIdx.x) * GEMM_TILE;
+    f32x16_t tot;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tot[v] = 0.f;
+    for (int z = 0; z < S; ++z) {
+        float4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] = *reinterpret_cast<const float4 *>(src + (size_t)z * ntiles * GEMM_TILE +
+                                                     gemm_part_offset(bb, q, tid));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            tot[4 * q] += v[q].x;
+            tot[4 * q + 1] += v[q].y;
+            tot[4 * q + 2] += v[q].z;
+            tot[4 * q + 3] += v[q].w;
+        }
+    }
+    const int nrow = blockIdx.x * GEMM_BN + 32 * w + (lane & 31);
+    gemm_store_block(tot, blockIdx.y * GEMM_BM + 32 * bb, lane >> 5, nrow, n, batch, post, y, ldy,
+                     ybf16, 0);
 }
 
 // Clears the fp32 rows y[b][0..n) (row stride ldy) before a split-k launch
@@ -298,25 +371,52 @@ __global__ void gemm_zero_kernel(float *__restrict__ y, int64_t batch, int n, in
     for (int64_t e = i; e < count; e += stride) y[(e / n) * ldy + e % n] = 0.f;
 }
 
-// Split k only when the output tiles leave most CUs idle; each split keeps
-// at least 8 groups (measured at batch 256: below that the fixed cost of a
-// workgroup and the fp32 atomic adds of its partial tile outweigh the CUs
-// gained -- o_proj 4096x4096 takes 36 us at 4 splits, 42 us at 8).
-static int gemm_splits(const QgemmArgs &a, int cu_count) {
-    const int tiles = (a.n + GEMM_BN - 1) / GEMM_BN * (int)((a.batch + GEMM_BM - 1) / GEMM_BM);
+// Split k only when the output tiles leave most CUs idle.  Each split keeps
+// at least min_groups groups: 8 when the splits meet through fp32 atomics
+// (measured at batch 256: below that the atomic adds of the partial tiles
+// outweigh the CUs gained), 4 when they meet in a workspace.
+static int gemm_tiles(const QgemmArgs &a) {
+    return (a.n + GEMM_BN - 1) / GEMM_BN * (int)((a.batch + GEMM_BM - 1) / GEMM_BM);
+}
+
+static int gemm_splits(const QgemmArgs &a, int cu_count, int min_groups) {
+    const int tiles = gemm_tiles(a);
     const int G = a.k / 128;
     int s = 1;
-    while (tiles * s * 2 <= cu_count && G / (2 * s) >= 8) s *= 2;
+    while (tiles * s * 2 <= cu_count && G / (2 * s) >= min_groups) s *= 2;
     return s;
+}
+
+constexpr int GEMM_WS_MIN_GROUPS = 4;
+constexpr int GEMM_ATOMIC_MIN_GROUPS = 8;
+
+// Splits that hold at least one group when each takes ceil(G / splits).
+static int gemm_live_splits(int G, int splits) {
+    const int gps = (G + splits - 1) / splits;
+    return (G + gps - 1) / gps;
+}
+
+// Workspace of the deterministic split: splits x tiles partial tiles of fp32.
+int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count) {
+    const int splits = gemm_live_splits(a.k / 128, gemm_splits(a, cu_count, GEMM_WS_MIN_GROUPS));
+    if (splits <= 1) return 0;
+    return (int64_t)splits * gemm_tiles(a) * GEMM_TILE * 4;
 }
 
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int G = a.k / 128;
-    // split-k adds fp32 partial sums into y: only for fp32 outputs
-    const int splits = a.ybf16 ? 1 : gemm_splits(a, cu_count);
-    const int gps = (G + splits - 1) / splits;
-    if (splits > 1) {
+    // With a large enough workspace the splits meet there (deterministic, any
+    // output type); without one they add fp32 partial sums into y (fp32 only).
+    const int64_t need = gemm_workspace_bytes(a, cu_count);
+    const bool use_ws = need > 0 && a.ws && a.ws_bytes >= need;
+    const int want = use_ws ? gemm_splits(a, cu_count, GEMM_WS_MIN_GROUPS)
+                            : (a.ybf16 ? 1 : gemm_splits(a, cu_count, GEMM_ATOMIC_MIN_GROUPS));
+    const int gps = (G + want - 1) / want;
+    const int splits = gemm_live_splits(G, want);
+    float *part = use_ws ? static_cast<float *>(a.ws) : nullptr;
+    const int atomic = splits > 1 && !use_ws ? 1 : 0;
+    if (atomic) {
         const int64_t count = a.batch * (int64_t)a.n;
         const int64_t blocks = (count + 255) / 256;
         hipLaunchKernelGGL(gemm_zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
@@ -325,13 +425,17 @@ static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const dim3 grid((a.n + GEMM_BN - 1) / GEMM_BN, (unsigned)((a.batch + GEMM_BM - 1) / GEMM_BM),
                     splits);
     if (a.zeros)
-        hipLaunchKernelGGL((gemm_kernel<R, true>), grid, dim3(64 * GEMM_WAVES), 0, stream, a.x,
+        hipLaunchKernelGGL((gemm_kernel<R, true>), grid, dim3(GEMM_THREADS), 0, stream, a.x,
                            a.ldx, (int)a.batch, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k,
-                           gps, a.y, a.ldy, a.ybf16, splits > 1 ? 1 : 0);
+                           gps, a.y, a.ldy, a.ybf16, atomic, part);
     else
-        hipLaunchKernelGGL((gemm_kernel<R, false>), grid, dim3(64 * GEMM_WAVES), 0, stream, a.x,
+        hipLaunchKernelGGL((gemm_kernel<R, false>), grid, dim3(GEMM_THREADS), 0, stream, a.x,
                            a.ldx, (int)a.batch, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k,
-                           gps, a.y, a.ldy, a.ybf16, splits > 1 ? 1 : 0);
+                           gps, a.y, a.ldy, a.ybf16, atomic, part);
+    if (part)
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3(grid.x, grid.y, 4 * GEMM_WAVES), dim3(64), 0,
+                           stream, part, splits, (int)a.batch, a.n, (float)(1 << (8 - R)), a.y,
+                           a.ldy, a.ybf16);
 }
 
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {

@@ -20,6 +20,8 @@ struct QgemmArgs {
     int64_t ldx = 0, ldy = 0;          // row strides in elements (set by the caller: >= k, >= n)
     int ybf16 = 0;                     // store Y as bf16 (round to nearest even)
     const uint16_t *zeros = nullptr;   // asymmetric: bf16 [n][k/128] zero points, else null
+    void *ws = nullptr;                // caller's workspace for split-k (zeroed before first use), or null
+    int64_t ws_bytes = 0;
 };
 
 // Y element store shared by the kernels: fp32, or bf16 rounded to nearest even.
@@ -49,6 +51,9 @@ hipError_t launch_unpack(int r, const uint8_t *planes, int64_t plane_bytes, int 
 hipError_t launch_gemv(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
+// Workspace bytes the large-batch GEMM uses to split k deterministically (0:
+// the launch does not split).
+int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count);
 
 // Plain streaming read of [src, src + bytes) (bytes a multiple of 16), one
 // XOR word per wave into sink (stream_sink_words() words).

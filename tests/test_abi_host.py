@@ -151,7 +151,21 @@ def test_qgemm_ex_validation(lib):
     assert call(opts(y_dtype=2)) == EUNSUPPORTED
     assert call(opts(kernel=9)) == EUNSUPPORTED
     assert call(opts(zeros_bf16=FAKE + 2)) == EALIGN
+    assert call(opts(workspace=FAKE, workspace_bytes=-1)) == EINVAL
+    assert call(opts(workspace=FAKE + 16, workspace_bytes=4096)) == EALIGN   # not 256-aligned
     assert call(opts(), b=0, x=0, y=0) == OK        # empty product
+
+
+def test_workspace_bytes_without_device_work(lib):
+    # Bad arguments and the kernels that never split answer without a device query.
+    assert lib.nbw_qgemm_workspace_bytes(-1, 4096, 4096, 4, 0) == -1
+    assert lib.nbw_qgemm_workspace_bytes(0, 4096, 4096, 4, 0) == 0     # empty batch: no launch
+    assert lib.nbw_qgemm_workspace_bytes(256, 4096, 100, 4, 0) == -1
+    assert lib.nbw_qgemm_workspace_bytes(256, 4096, 4096, 9, 0) == -1
+    assert lib.nbw_qgemm_workspace_bytes(256, 4096, 4096, 4, 7) == -1
+    assert lib.nbw_qgemm_workspace_bytes(1, 4096, 4096, 4, 0) == 0     # GEMV
+    assert lib.nbw_qgemm_workspace_bytes(16, 4096, 4096, 4, 0) == 0    # small-batch kernel
+    assert lib.nbw_qgemm_workspace_bytes(256, 4096, 4096, 4, 2) == 0   # forced small-batch kernel
 
 
 def test_choose_codes_validation(lib):
