@@ -238,6 +238,53 @@ __host__ __device__ __forceinline__ void decode_word(const uint32_t *P, uint32_t
     if constexpr (Phases<R>::count == 2) decode_phase<Phases<R>::rp1, 0>(P + 4, D1);
 }
 
+// Single-phase decode for R = 5..8 (the large-batch GEMM): each column's
+// child code as one bf16 integer, q * 2^(8-R) (at most 8 significant bits,
+// so exact; the two-phase decode above needs two MFMA operands per column).
+// Planes 0..3 and 4..7 (those at or past R read as zero) go through the
+// four-plane network; one byte-level merge per word then joins the two
+// nibbles of each position into its code byte (high nibble from planes
+// 0..3), and byte k of a word converts to fp32 exactly, whose top half is
+// the bf16 value.  Output D[m] = bf16 pair (column 2m, column 2m+1), i.e.
+// positions m and m + 16 of the plane words.
+// bf16 pair (lo, hi) from two fp32 values whose low 16 bits are zero: the
+// top halves of their bit patterns.
+__host__ __device__ __forceinline__ uint32_t pair_of_f32_tops(float lo, float hi) {
+    const uint32_t l = __builtin_bit_cast(uint32_t, lo), h = __builtin_bit_cast(uint32_t, hi);
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_perm(h, l, 0x07060302u);
+#else
+    return (h & 0xFFFF0000u) | (l >> 16);
+#endif
+}
+
+template <int R>
+__host__ __device__ __forceinline__ void decode_word_bytes(const uint32_t *P, uint32_t *D) {
+    static_assert(R >= 5 && R <= 8, "byte decode is for 5..8 planes");
+    uint32_t Ph[4] = {P[0], P[1], P[2], P[3]};
+    uint32_t Pl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) Pl[p] = 4 + p < R ? P[4 + p] : 0u;
+    uint32_t Zh[4], Zl[4];
+    network<4>(Ph, Zh);
+    network<4>(Pl, Zl);
+    // BH[s] byte k: code of position 4(2k+1) + s; BL[s] byte k: position 8k + s.
+    uint32_t BH[4], BL[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) merge(Zh[s], Zl[s], 4, M4, BH[s], BL[s]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int s = m & 3, j = m >> 2;  // position m: nibble j of word s; m + 16: nibble j + 4
+        const uint32_t wlo = (j & 1) ? BH[s] : BL[s];
+        const int blo = (j & 1) ? (j - 1) >> 1 : j >> 1;
+        const uint32_t whi = (j & 1) ? BH[s] : BL[s];
+        const int bhi = (j & 1) ? (j + 3) >> 1 : (j + 4) >> 1;
+        const float flo = (float)((wlo >> (8 * blo)) & 0xFFu);
+        const float fhi = (float)((whi >> (8 * bhi)) & 0xFFu);
+        D[m] = pair_of_f32_tops(flo, fhi);
+    }
+}
+
 // Raw codes (no bf16) of pair m for an RP-plane phase: low half and high half.
 template <int RP>
 __host__ __device__ __forceinline__ uint32_t extract_codes(const uint32_t *Z, int m) {

@@ -89,6 +89,26 @@ __device__ __forceinline__ int gemm_part_offset(int bb, int q, int tid) {
     return ((bb * 4 + q) * GEMM_THREADS + tid) * 4;
 }
 
+// Sum over the four lanes of a quad (lanes 4i..4i+3), in every lane: two
+// DPP quad permutes, no LDS round trip.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+    return v;
+}
+
+// Operand form per child width.  R <= 4: the one-phase magic-exponent
+// decode, operand offset_m + q with the offsets removed by the correction,
+// result scaled by 2^(8-R) at the end.  R = 5..8: the single-phase byte
+// decode, operand q * 2^(8-R) (exact in bf16), one correction coefficient
+// (1/2 - 2^(R-1)) * 2^(8-R) for every column, no final scaling.  Either way
+// one MFMA per k-step.
+template <int R> struct GemmOperand {
+    static constexpr bool bytes = R > 4;
+    static constexpr float post = bytes ? 1.0f : (float)(1 << (8 - R));
+    static constexpr float byte_coef = (0.5f - (float)(1 << (R - 1))) * (float)(1 << (8 - R));
+};
+
 // grid: (ceil(n / 256), ceil(batch / 128), splits); block 512.  Groups
 // [z * gps, min(G, (z + 1) * gps)) of k.  Split k (splits > 1) either adds
 // fp32 partial sums into y with atomics (atomic != 0; the launcher has
@@ -96,8 +116,9 @@ __device__ __forceinline__ int gemm_part_offset(int bb, int q, int tid) {
 // tile there for gemm_reduce_kernel to add in a fixed order.  ASYM:
 // asymmetric children, zeros bf16 [n][k/128]: each weight gains
 // s * (127.5 - z) over the symmetric child, i.e. the product gains
-// s * (127.5 - z) * 2^(R-8) * (group sum of the batch row's X), added through
-// the same fp32 product as the corrections.
+// s * (127.5 - z) * (group sum of the batch row's X), added through the same
+// fp32 product as the corrections (in accumulator units: divided by the
+// final scaling GemmOperand<R>::post).
 template <int R, bool ASYM>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int batch, const uint8_t *__restrict__ planes,
@@ -109,7 +130,8 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     // while group g runs, the pair (g-2, g-1) is read and g+1 is staged
     __shared__ __align__(16) float corr[4][GEMM_BM];
     __shared__ __align__(16) float xsum[ASYM ? 4 : 1][GEMM_BM];
-    constexpr int NPH = Phases<R>::count;
+    constexpr bool BYTES = GemmOperand<R>::bytes;
+    constexpr float POST = GemmOperand<R>::post;
 
     const int G = k >> 7;
     const int g_begin = blockIdx.z * gps;
@@ -141,30 +163,41 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
             xv[c] = *reinterpret_cast<const u32x4_t *>(xrow + 128 * g + 8 * c);
     };
     auto stage_x = [&](int buf, int slot) {
-        const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
-        float cpart = 0.f;
+        uint32_t xw[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             *reinterpret_cast<u32x4_t *>(&xs[buf][xr * GEMM_XSTRIDE + 32 * qq + 8 * c]) = xv[c];
-            cpart = fmaf(pair_coef<R>(4 * c + 0), gm_dot2(one, xv[c].x, 0.f), cpart);
-            cpart = fmaf(pair_coef<R>(4 * c + 1), gm_dot2(one, xv[c].y, 0.f), cpart);
-            cpart = fmaf(pair_coef<R>(4 * c + 2), gm_dot2(one, xv[c].z, 0.f), cpart);
-            cpart = fmaf(pair_coef<R>(4 * c + 3), gm_dot2(one, xv[c].w, 0.f), cpart);
+            xw[4 * c] = xv[c].x;
+            xw[4 * c + 1] = xv[c].y;
+            xw[4 * c + 2] = xv[c].z;
+            xw[4 * c + 3] = xv[c].w;
         }
-        cpart += __shfl_xor(cpart, 1);
-        cpart += __shfl_xor(cpart, 2);
+        // This thread's share of the row's correction (pairs m = 0..15 of
+        // word qq), then the sum over the row's four threads (one quad).
+        float own;
+        if constexpr (BYTES) {
+            const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
+            float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; m += 2) {
+                c0 = gm_dot2(one, xw[m], c0);
+                c1 = gm_dot2(one, xw[m + 1], c1);
+            }
+            own = GemmOperand<R>::byte_coef * (c0 + c1);
+        } else {
+            own = correction<R, 16>(xw);
+        }
+        const float cpart = quad_sum(own);
         if (qq == 0) corr[slot][xr] = cpart;
         if constexpr (ASYM) {
-            float sx = 0.f;
+            const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
+            float sx0 = 0.f, sx1 = 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                sx = gm_dot2(one, xv[c].x, sx);
-                sx = gm_dot2(one, xv[c].y, sx);
-                sx = gm_dot2(one, xv[c].z, sx);
-                sx = gm_dot2(one, xv[c].w, sx);
+            for (int m = 0; m < 16; m += 2) {
+                sx0 = gm_dot2(one, xw[m], sx0);
+                sx1 = gm_dot2(one, xw[m + 1], sx1);
             }
-            sx += __shfl_xor(sx, 1);
-            sx += __shfl_xor(sx, 2);
+            const float sx = quad_sum(sx0 + sx1);
             if (qq == 0) xsum[slot][xr] = sx;
         }
     };
@@ -221,39 +254,47 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     for (int g = g_begin; g < g_end; ++g) {
         const int buf = (g - g_begin) & 1;
         const int slot = (g - g_begin) & 3;
+        // X of the next group first, ahead of everything else in the group:
+        // it is staged at the group's end and should arrive well before.
+        // Loads retire in order, so staging X then waits only for X (an L2
+        // hit), not for the planes coming from HBM.  The loads are
+        // unconditional (clamped to the last group), so the number in flight
+        // behind X is static and the compiler's wait for X stays exact.
+        const int gn = min(g + 1, g_end - 1);
+        load_x(gn);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // Decode this group's weight operands: Bop[ph][pair].
-        uint32_t Bop[NPH][32];
+        // Decode this group's weight operands: Bop[pair].
+        uint32_t Bop[32];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             uint32_t P[R];
 #pragma unroll
             for (int p = 0; p < R; ++p) P[p] = q ? pw[p].y : pw[p].x;
-            uint32_t D0[16], D1[16];
-            decode_word<R>(P, D0, D1);
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                Bop[0][16 * q + m] = D0[m];
-                if constexpr (NPH == 2) Bop[NPH - 1][16 * q + m] = D1[m];
+            if constexpr (BYTES) {
+                decode_word_bytes<R>(P, Bop + 16 * q);
+            } else {
+                uint32_t D1[16];
+                decode_word<R>(P, Bop + 16 * q, D1);
             }
         }
-        const float s = nrow < n ? __uint_as_float(sraw << 16) : 0.f;
-        const float zc = ASYM ? (127.5f - __uint_as_float(zraw << 16)) *
-                                    (1.0f / (float)(1 << (8 - R)))
-                              : 0.f;
+        float s = nrow < n ? __uint_as_float(sraw << 16) : 0.f;
+        float zc = ASYM ? (127.5f - __uint_as_float(zraw << 16)) *
+                              (1.0f / POST)
+                        : 0.f;
+        // Materialise them here, before sraw / zraw are reloaded: computed
+        // after the reload, the old values would need a register copy at the
+        // loop's end, and a copy waits for every load in flight (the planes
+        // from HBM included).
+        asm volatile("" : "+v"(s));
+        if constexpr (ASYM) asm volatile("" : "+v"(zc));
         // Groups g-2, g-1 form a finished pair: their corrections go in now,
         // next to this group's decode (their slots are not written again
         // before the barrier after group g+1).
         if (g - g_begin >= 2 && ((g - g_begin) & 1) == 0)
             correct(h ? (slot + 3) & 3 : (slot + 2) & 3, h ? s_prev : s_prev2, h ? zs_prev : zs_prev2);
 
-        // Fetch X and the planes of the next group.  X goes first: loads
-        // retire in order, so staging X then waits only for X (an L2 hit),
-        // not for the planes coming from HBM.  The loads are unconditional
-        // (clamped to the last group), so the number in flight behind X is
-        // static and the compiler's wait for X stays exact.
-        const int gn = min(g + 1, g_end - 1);
-        load_x(gn);
+        // The planes of the next group.
         load_w(gn);
 
 #pragma unroll
@@ -271,12 +312,8 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
                     const int bb = 2 * bp + e;
                     const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
                         &xs[buf][(32 * bb + l32) * GEMM_XSTRIDE + 64 * h + 8 * j]);
-#pragma unroll
-                    for (int ph = 0; ph < NPH; ++ph) {
-                        const u32x4_t wv = {Bop[ph][4 * j], Bop[ph][4 * j + 1], Bop[ph][4 * j + 2],
-                                            Bop[ph][4 * j + 3]};
-                        Pc[e] = gm_mfma(a, wv, Pc[e]);
-                    }
+                    const u32x4_t wv = {Bop[4 * j], Bop[4 * j + 1], Bop[4 * j + 2], Bop[4 * j + 3]};
+                    Pc[e] = gm_mfma(a, wv, Pc[e]);
                 }
             }
 #pragma unroll
@@ -290,6 +327,9 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
         s_prev = s;
         zs_prev = ASYM ? s * zc : 0.f;
 
+        // (kept after the MFMAs: scheduled among them, the staging's reads
+        // of X would stall the chains on the X loads)
+        __builtin_amdgcn_sched_barrier(0);
         stage_x(buf ^ 1, (slot + 1) & 3);  // (past the end: a repeat of the last group, never read)
         __syncthreads();
     }
@@ -320,10 +360,9 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     }
 
     // Epilogue: lane holds rows b0 + 32bb + 8(v/4) + 4h + v%4 of column nrow.
-    const float post = (float)(1 << (8 - R));
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
-        gemm_store_block(acc[bb], b0 + 32 * bb, h, nrow, n, batch, post, y, ldy, ybf16, atomic);
+        gemm_store_block(acc[bb], b0 + 32 * bb, h, nrow, n, batch, POST, y, ldy, ybf16, atomic);
 }
 
 // Adds the S partial tiles of a split launch in the order z = 0..S-1 and
@@ -434,7 +473,7 @@ static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
                            gps, a.y, a.ldy, a.ybf16, atomic, part);
     if (part)
         hipLaunchKernelGGL(gemm_reduce_kernel, dim3(grid.x, grid.y, 4 * GEMM_WAVES), dim3(64), 0,
-                           stream, part, splits, (int)a.batch, a.n, (float)(1 << (8 - R)), a.y,
+                           stream, part, splits, (int)a.batch, a.n, GemmOperand<R>::post, a.y,
                            a.ldy, a.ybf16);
 }
 

@@ -1,7 +1,9 @@
 // Host-side harness for the library's bit-plane network (decode.h): runs the
 // same pack / decode / extraction functions the kernels inline, on the CPU, with
 // the kernels' chunk indexing, so tests can compare them with the oracle
-// without a GPU.  Usage: decode_harness <pack|unpack|operands> n k r in out
+// without a GPU.  Usage: decode_harness <pack|unpack|operands|bytes> n k r in out
+// (bytes: the single-phase operands of the large-batch GEMM, r = 5..8, divided
+// by 2^(8-r))
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -16,6 +18,31 @@ static float bf16f(uint32_t h) {
     float f;
     std::memcpy(&f, &u, 4);
     return f;
+}
+
+template <int R>
+static void byte_operands(const std::vector<uint8_t> &planes, int n, int k, std::vector<float> &vals) {
+    if constexpr (R >= 5) {
+        const int G = k / 128;
+        const int64_t pb = (int64_t)((n + 15) / 16) * 16 * (k / 8);
+        const float unit = (float)(1 << (8 - R));
+        for (int row = 0; row < n; ++row)
+            for (int g = 0; g < G; ++g) {
+                const int64_t chunk = ((int64_t)(row / 16) * G + g) * 16 + row % 16;
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t P[8] = {0};
+                    for (int p = 0; p < R; ++p)
+                        std::memcpy(&P[p], &planes[p * pb + chunk * 16 + 4 * d], 4);
+                    uint32_t D[16];
+                    decode_word_bytes<R>(P, D);
+                    for (int m = 0; m < 16; ++m) {
+                        const int64_t col = (int64_t)g * 128 + 32 * d + 2 * m;
+                        vals[(int64_t)row * k + col] = bf16f(D[m]) / unit;
+                        vals[(int64_t)row * k + col + 1] = bf16f(D[m] >> 16) / unit;
+                    }
+                }
+            }
+    }
 }
 
 template <int R>
@@ -93,6 +120,16 @@ int main(int argc, char **argv) {
                     }
                 }
         fwrite(planes.data(), 1, planes.size(), fo);
+    } else if (!strcmp(mode, "bytes")) {
+        std::vector<float> vals((size_t)n * k);
+        switch (r) {
+        case 5: byte_operands<5>(in, n, k, vals); break;
+        case 6: byte_operands<6>(in, n, k, vals); break;
+        case 7: byte_operands<7>(in, n, k, vals); break;
+        case 8: byte_operands<8>(in, n, k, vals); break;
+        default: return 5;
+        }
+        fwrite(vals.data(), 4, vals.size(), fo);
     } else {
         const bool operands = !strcmp(mode, "operands");
         std::vector<uint8_t> codes((size_t)n * k);

@@ -2,9 +2,9 @@
 
 tests/native/decode_harness.hip compiles decode.h -- the very functions the
 kernels inline -- for the host and applies them with the kernels' chunk
-indexing.  This checks the packer network, the unpack network and the bf16
-operand decode (magic exponents, offsets, coefficients) bit for bit without a
-GPU.
+indexing.  This checks the packer network, the unpack network, the bf16
+operand decode (magic exponents, offsets, coefficients) and the single-phase
+byte decode of the large-batch GEMM bit for bit without a GPU.
 """
 import os
 import subprocess
@@ -61,4 +61,14 @@ def test_bf16_operands_decode_to_codes(harness, tmp_path, r):
     codes = synth.uniform_codes(n, k, np.random.default_rng(22 + r))
     planes = oracle.pack(codes)
     got = np.frombuffer(_run(harness, "operands", n, k, r, planes, tmp_path), dtype=np.float32)
+    np.testing.assert_array_equal(got.reshape(n, k), oracle.unpack(planes, n, k, r).astype(np.float32))
+
+
+@pytest.mark.parametrize("r", range(5, 9))
+def test_byte_operands_decode_to_codes(harness, tmp_path, r):
+    # the single-phase bf16 operand is the child code times 2^(8-r), exactly
+    n, k = 19, 384
+    codes = synth.uniform_codes(n, k, np.random.default_rng(40 + r))
+    planes = oracle.pack(codes)
+    got = np.frombuffer(_run(harness, "bytes", n, k, r, planes, tmp_path), dtype=np.float32)
     np.testing.assert_array_equal(got.reshape(n, k), oracle.unpack(planes, n, k, r).astype(np.float32))
