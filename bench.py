@@ -490,7 +490,9 @@ def main():
         nbw.choose_codes(wf, Lg["s"][0])
         cms = event_time(torch, lambda i: nbw.choose_codes(wf, Lg["s"][0]), 3)
         nweights = Lg["n"] * Lg["k"]
-        ops = nweights * 256 * 3 * 8  # fp64 operations per weight: 256 codes x 3 widths x 8
+        # fp64 arithmetic per (code, width): q + 1/2, - 2^(r-1), x s*2^(8-r), w - d, square,
+        # x lambda, + loss (7; s*2^(8-r) is per weight and width, q's conversion is not counted)
+        ops = nweights * 256 * 3 * 7
         result["choose_codes"] = {
             "weights_per_s": round(nweights / (cms * 1e-3), 1), "ms": round(cms, 3),
             "shape": [Lg["n"], Lg["k"]], "widths": [3, 4, 8],
