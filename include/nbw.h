@@ -242,6 +242,52 @@ nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, v
 int32_t nbw_stream_sink_words(void);
 nbw_status nbw_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
+/* On-disk form of a sliceable parent (host only, no device work).  The r-bit
+ * child loads exactly r bits per weight (MatGPTQ: Efficient and Accurate
+ * Inference over Nested Quantized Models, Abstract; Table 1, row "Exact r-bit
+ * loading"), so the file keeps the scales ahead of the planes and the planes
+ * MSB first: the first nbw_file_prefix_bytes(n, k, r) bytes of a parent file
+ * hold everything an r-bit child needs, and a file cut after them is itself a
+ * valid child file.  Layout (integers little-endian):
+ *   [0, NBW_FILE_HEADER_BYTES)  header, written by nbw_file_header
+ *   scales_offset               bf16 scales [n][k/128] row-major
+ *   planes_offset               plane p at planes_offset + p*plane_bytes
+ *                               (p = 0..7, plane 0 = MSB), byte for byte the
+ *                               device layout NBW_LAYOUT_T16
+ * planes_offset = NBW_FILE_HEADER_BYTES + the scale bytes rounded up to a
+ * multiple of 4096. */
+#define NBW_FILE_HEADER_BYTES 4096
+
+typedef struct nbw_file_info {
+    int64_t n, k;
+    int32_t nplanes;        /* planes the writer stored (8 for a parent) */
+    int32_t layout;         /* NBW_LAYOUT_T16 */
+    int64_t plane_bytes;    /* nbw_plane_bytes(n, k) */
+    int64_t scales_offset;  /* NBW_FILE_HEADER_BYTES */
+    int64_t scales_bytes;   /* n * (k/128) * 2 */
+    int64_t planes_offset;
+    int32_t planes_present; /* whole planes within the first file_bytes bytes (0..nplanes) */
+    int32_t reserved;
+} nbw_file_info;
+
+/* Bytes of a parent file's prefix that holds the header, the scales and
+ * planes 0..r-1 (r = 0..8; r = 0 gives planes_offset), or -1 on bad input. */
+int64_t nbw_file_prefix_bytes(int64_t n, int64_t k, int32_t r);
+
+/* Writes the NBW_FILE_HEADER_BYTES-byte header of an 8-plane parent file for
+ * an n x k matrix into the host buffer header_out (caller-owned).
+ * Errors: NBW_EINVAL (null buffer, bad shape). */
+nbw_status nbw_file_header(int64_t n, int64_t k, void *header_out);
+
+/* Checks a header (host buffer of NBW_FILE_HEADER_BYTES bytes) and describes
+ * the file, given that its first file_bytes bytes are available (the whole
+ * file, or a prefix of it): info->planes_present says how many whole planes
+ * that prefix holds, so a child of r <= planes_present can be loaded.
+ * Errors: NBW_EINVAL (null pointer, wrong magic or header size, a field that
+ * disagrees with the layout), NBW_EUNSUPPORTED (unknown layout, scale type or
+ * group size), NBW_ERANGE (the prefix ends before the planes start). */
+nbw_status nbw_file_parse(const void *header, int64_t file_bytes, nbw_file_info *info);
+
 /* Name of the kernel template instance nbw_qgemm_kernel would launch for
  * this problem on the current device (for example "nbw::gemv_kernel<4, 1, 2>",
  * as profilers print it without the parameter list), or "" on bad input.  The

@@ -58,12 +58,23 @@ class Problem(ctypes.Structure):
                 ("scales_bf16", ctypes.c_void_p), ("r", ctypes.c_int32), ("y", ctypes.c_void_p)]
 
 
+class FileInfo(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("nplanes", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("plane_bytes", ctypes.c_int64),
+                ("scales_offset", ctypes.c_int64), ("scales_bytes", ctypes.c_int64),
+                ("planes_offset", ctypes.c_int64), ("planes_present", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+FILE_HEADER_BYTES = 4096
+
 _LIB = None
 
 EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
            "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex",
            "nbw_qgemm_workspace_bytes", "nbw_qgemm_grouped",
            "nbw_choose_codes", "nbw_unpack_codes", "nbw_stream_sink_words", "nbw_stream_read",
+           "nbw_file_prefix_bytes", "nbw_file_header", "nbw_file_parse",
            "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
 
 
@@ -112,6 +123,12 @@ def _lib():
         lib.nbw_kernel_name.restype = ctypes.c_char_p
         lib.nbw_version.argtypes = []
         lib.nbw_version.restype = ctypes.c_char_p
+        lib.nbw_file_prefix_bytes.argtypes = [i64, i64, i32]
+        lib.nbw_file_prefix_bytes.restype = i64
+        lib.nbw_file_header.argtypes = [i64, i64, vp]
+        lib.nbw_file_header.restype = ctypes.c_int
+        lib.nbw_file_parse.argtypes = [vp, i64, ctypes.POINTER(FileInfo)]
+        lib.nbw_file_parse.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -439,6 +456,73 @@ def stream_read(src: torch.Tensor, nbytes: int, sink: torch.Tensor) -> None:
                                   ctypes.c_void_p(sink.data_ptr()), _stream(src)), "nbw_stream_read")
 
 
+def file_prefix_bytes(n: int, k: int, r: int) -> int:
+    """Bytes at the head of a parent file that hold everything an r-bit child needs."""
+    v = _lib().nbw_file_prefix_bytes(n, k, r)
+    if v < 0:
+        raise ValueError(f"bad shape or bit-width n={n}, k={k}, r={r}")
+    return int(v)
+
+
+def save_parent(path, w: PackedWeight, scales: torch.Tensor) -> None:
+    """Write the 8-plane parent ``w`` and its bf16 scales [n][k/128] to ``path``
+    (header, scales, planes 0..7: the library's file layout, whose r-bit child is
+    the file's first ``file_prefix_bytes(n, k, r)`` bytes).  The planes and scales
+    may live on the GPU or on the host; they are copied to the host to be written."""
+    if w.nplanes != 8:
+        raise ValueError("save_parent needs the 8-plane parent")
+    if not isinstance(scales, torch.Tensor) or scales.dtype != torch.bfloat16:
+        raise ValueError("scales must be a bf16 tensor (host or device)")
+    if tuple(scales.shape) != (w.n, w.k // 128):
+        raise ValueError(f"scales must be [{w.n}][{w.k // 128}]")
+    hdr = ctypes.create_string_buffer(FILE_HEADER_BYTES)
+    _check(_lib().nbw_file_header(w.n, w.k, hdr), "nbw_file_header")
+    info = FileInfo()
+    _check(_lib().nbw_file_parse(hdr, file_prefix_bytes(w.n, w.k, 8), ctypes.byref(info)),
+           "nbw_file_parse")
+    sbytes = scales.contiguous().view(torch.uint8).reshape(-1).cpu().numpy().tobytes()
+    planes = w.storage[: 8 * w.plane_bytes].cpu().numpy().tobytes()
+    with open(path, "wb") as f:
+        f.write(hdr.raw)
+        f.write(sbytes)
+        f.write(b"\0" * (info.planes_offset - info.scales_offset - len(sbytes)))
+        f.write(planes)
+
+
+def file_info(path) -> FileInfo:
+    """Header of a parent (or child) file, checked, with the planes its size holds."""
+    with open(path, "rb") as f:
+        hdr = f.read(FILE_HEADER_BYTES)
+    if len(hdr) < FILE_HEADER_BYTES:
+        raise ValueError(f"{path}: shorter than a header")
+    info = FileInfo()
+    _check(_lib().nbw_file_parse(hdr, os.path.getsize(path), ctypes.byref(info)), "nbw_file_parse")
+    return info
+
+
+def load_child(path, r: int, device="cuda"):
+    """The r-bit child of the parent stored in ``path``: reads only the file's first
+    ``file_prefix_bytes(n, k, r)`` bytes (header, scales, planes 0..r-1).  Returns
+    (PackedWeight with r planes, bf16 scales [n][k/128]) on ``device``."""
+    info = file_info(path)
+    if not 1 <= r <= info.planes_present:
+        raise ValueError(f"{path}: r={r} needs {r} planes, the file holds {info.planes_present}")
+    n, k = int(info.n), int(info.k)
+    with open(path, "rb") as f:
+        f.seek(info.scales_offset)
+        sb = f.read(info.scales_bytes)
+        f.seek(info.planes_offset)
+        pb = f.read(r * info.plane_bytes)
+    if len(sb) != info.scales_bytes or len(pb) != r * info.plane_bytes:
+        raise ValueError(f"{path}: short read")
+    # fresh tensors on the device (aligned as the views require), filled from the bytes read
+    scales = torch.empty((n, k // 128), dtype=torch.bfloat16, device=device)
+    scales.view(torch.uint8).reshape(-1).copy_(torch.frombuffer(bytearray(sb), dtype=torch.uint8))
+    planes = torch.empty(r * info.plane_bytes, dtype=torch.uint8, device=device)
+    planes.copy_(torch.frombuffer(bytearray(pb), dtype=torch.uint8))
+    return PackedWeight(planes, n, k, r), scales
+
+
 def kernel_name(batch: int, n: int, k: int, r: int, kernel: str = "auto") -> str:
     """Name of the kernel instance nbw_qgemm would launch (as profilers print it)."""
     return _lib().nbw_kernel_name(batch, n, k, r, KERNELS[kernel]).decode()
@@ -448,6 +532,7 @@ def version() -> str:
     return _lib().nbw_version().decode()
 
 
-__all__ = ["pack_bitplanes", "slice_view", "qgemm", "QgemmCall", "qgemm_grouped", "workspace_bytes", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "plane_bytes",
+__all__ = ["pack_bitplanes", "slice_view", "save_parent", "load_child", "file_info",
+           "file_prefix_bytes", "qgemm", "QgemmCall", "qgemm_grouped", "workspace_bytes", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]
