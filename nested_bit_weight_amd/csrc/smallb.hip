@@ -13,9 +13,13 @@
 //    of the activations; the k-slot order inside a quarter only has to agree
 //    between the two operands, so each lane feeds its decoded plane word in
 //    the order the decoder produces it (pairs 4j..4j+3 -> MFMA j).
-//  - lane (row c, quarter d) of a wave loads 32-bit word d of its row's
-//    16-byte chunk of each plane: one wave load covers the 256 contiguous
-//    bytes of a 16-row tile of one group.
+//  - lane (row c, quarter d) of a wave loads the whole 16-byte chunk of row c
+//    of group 4*set + d for each plane (one wave load covers the 1 KB of a
+//    16-row tile's four groups), and a 4 x 4 transpose across the quarter
+//    lanes (v_permlane16_swap, v_permlane32_swap) then leaves in lane (c, d)
+//    word d of row c's chunk of every group of the set.  (Loading those words
+//    directly takes four times the load instructions, and the texture
+//    addresser's time went with the count of instructions, not of bytes.)
 //  - a workgroup owns a run of T 16-row tiles and all of k (about one
 //    workgroup per CU); its waves split k into 4-group sets (wave w: sets w,
 //    w+W, ...).  For each of its sets a wave loads the set's activation
@@ -40,6 +44,23 @@ constexpr int SMALLB_MAX_TILES = 16; // tiles per workgroup
 constexpr int SMALLB_DEPTH = 2;      // steps of planes in flight per wave
 
 __device__ __forceinline__ float sb_bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// 4 x 4 transpose across the four 16-lane rows of a wave: on entry, register
+// q of lane (c, row d) holds element (d, q); on exit, register q holds
+// element (q, d).  permlane16_swap exchanges odd rows of its first operand
+// with even rows of its second; permlane32_swap the first operand's upper
+// half with the second's lower half.
+__device__ __forceinline__ void sb_quad_transpose(uint32_t &r0, uint32_t &r1, uint32_t &r2,
+                                                  uint32_t &r3) {
+    const auto a = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
+    const auto e = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+    const auto f = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+    r0 = e[0];
+    r1 = f[0];
+    r2 = e[1];
+    r3 = f[1];
+}
 
 // Dynamic LDS: fp32 [W][T][4][64] partial sums (tile t, output v of lane l).
 __host__ __device__ constexpr size_t smallb_lds_bytes(int waves, int slots) {
@@ -76,7 +97,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) slot[(t * 4 + v) * 64 + lane] = 0.f;
 
-    // Step loads: for each of the set's 4 groups, the lane's plane words;
+    // Step loads: the lane's 16-byte plane chunks (group 4*set + d);
     // for each of the lane's 4 output rows (4d + v), the scales (and zero
     // points) of the 4 groups.
     uint32_t pl[PD][4][R];
@@ -115,14 +136,20 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
                 }
             }
         }
+        // row c's chunk of group 4*set + d, words q = 0..3 in pl[j][q][p]
+        // (transposed across the quarter lanes just before the decode)
+        {
+            const int g = min(4 * set + d, G - 1);
+            const uint8_t *base = planes + (((int64_t)tile * G + g) * 16 + c) * 16;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-            const int g = min(4 * set + gi, G - 1);
-            const uint8_t *base = planes + (((int64_t)tile * G + g) * 16 + c) * 16 + 4 * d;
-#pragma unroll
-            for (int p = 0; p < R; ++p)
-                pl[j][gi][p] = __builtin_nontemporal_load(
-                    reinterpret_cast<const uint32_t *>(base + p * plane_bytes));
+            for (int p = 0; p < R; ++p) {
+                const u32x4_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t *>(base + p * plane_bytes));
+                pl[j][0][p] = v.x;
+                pl[j][1][p] = v.y;
+                pl[j][2][p] = v.z;
+                pl[j][3][p] = v.w;
+            }
         }
     };
 
@@ -169,6 +196,9 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     };
 
     auto compute = [&](int j) {
+        // now pl[j][gi][p] = word d of row c's chunk of group 4*set + gi
+#pragma unroll
+        for (int p = 0; p < R; ++p) sb_quad_transpose(pl[j][0][p], pl[j][1][p], pl[j][2][p], pl[j][3][p]);
         f32x4_t out = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
