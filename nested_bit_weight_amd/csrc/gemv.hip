@@ -54,6 +54,18 @@ __host__ __device__ constexpr size_t gemv_lds_bytes(int waves, int slots) {
     return (size_t)waves * 1024 + (size_t)waves * slots * 64 * 4;
 }
 
+// Sum over each 16-lane row of the wave, in every lane of the row: DPP quad
+// permutes [1,0,3,2] and [2,3,0,1], then row_half_mirror (lane i of each
+// half-row reads lane 7-i: the other quad) and row_mirror (lane i reads
+// lane 15-i: the other half).  VALU only, no LDS round trip.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -163,19 +175,8 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
             float sx = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) sx = dot2(one, xw[64 * gg + i + 16 * q], sx);
-            float v = my_coef * sx;
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
-            cg = v;
-            if constexpr (ASYM) {
-                sx += __shfl_xor(sx, 1);
-                sx += __shfl_xor(sx, 2);
-                sx += __shfl_xor(sx, 4);
-                sx += __shfl_xor(sx, 8);
-                sg = sx;
-            }
+            cg = row16_sum(my_coef * sx);
+            if constexpr (ASYM) sg = row16_sum(sx);
         }
         // four independent dot2 chains (one per 32-column word) keep a wave's
         // dependent-issue latency off the critical path

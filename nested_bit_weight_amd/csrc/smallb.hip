@@ -45,6 +45,18 @@ constexpr int SMALLB_DEPTH = 2;      // steps of planes in flight per wave
 
 __device__ __forceinline__ float sb_bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Sum over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every
+// lane, as (row0 + row1) + (row2 + row3): one permlane16_swap and one
+// permlane32_swap of a value with itself give each lane its partner rows.
+__device__ __forceinline__ float sb_cross_row_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t us = __float_as_uint(s);
+    const auto b = __builtin_amdgcn_permlane32_swap(us, us, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 4 x 4 transpose across the four 16-lane rows of a wave: on entry, register
 // q of lane (c, row d) holds element (d, q); on exit, register q holds
 // element (q, d).  permlane16_swap exchanges odd rows of its first operand
@@ -176,10 +188,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-            float corr = correction<R, 16>(XB[gi]);
-            corr += __shfl_xor(corr, 16);
-            corr += __shfl_xor(corr, 32);
-            init[gi] = corr;
+            init[gi] = sb_cross_row_sum(correction<R, 16>(XB[gi]));
             if constexpr (ASYM) {
                 const uint32_t one = 0x3F803F80u;
                 float sx = 0.f;
@@ -188,9 +197,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
                     sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
                                                          __builtin_bit_cast(bf16x2_t, XB[gi][m]), sx,
                                                          false);
-                sx += __shfl_xor(sx, 16);
-                sx += __shfl_xor(sx, 32);
-                xsum[gi] = sx;
+                xsum[gi] = sb_cross_row_sum(sx);
             }
         }
     };
