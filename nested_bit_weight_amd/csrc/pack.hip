@@ -32,16 +32,32 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     const int gcount = min(PACK_GROUPS, G - g0);
     const int tid = threadIdx.x;
 
-    // Phase 1: 16 rows x (gcount*128) bytes into LDS, 16 bytes per load.
+    // Phase 1: 16 rows x (gcount*128) bytes into LDS, 16 bytes per load.  A
+    // full region is 8 loads per thread, all issued before the first LDS
+    // write (a load-wait-write loop would pay the memory latency 8 times).
     const int vec_per_row = gcount * 8;
-    for (int u = tid; u < 16 * vec_per_row; u += 256) {
+    auto load16 = [&](int u) {
         const int i = u / vec_per_row, v = u % vec_per_row;
         const int row = tile * 16 + i;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        u32x4_t val = {0u, 0u, 0u, 0u};
         if (row < n)
-            val = *reinterpret_cast<const uint4 *>(codes + (int64_t)row * k + (int64_t)g0 * 128 +
-                                                   16 * v);
-        *reinterpret_cast<uint4 *>(lds + i * PACK_ROW_BYTES + 16 * v) = val;
+            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                codes + (int64_t)row * k + (int64_t)g0 * 128 + 16 * v));
+        return val;
+    };
+    auto put16 = [&](int u, const u32x4_t &val) {
+        const int i = u / vec_per_row, v = u % vec_per_row;
+        *reinterpret_cast<u32x4_t *>(lds + i * PACK_ROW_BYTES + 16 * v) = val;
+    };
+    if (gcount == PACK_GROUPS) {
+        constexpr int PER = 16 * PACK_GROUPS * 8 / 256;
+        u32x4_t val[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) val[q] = load16(tid + 256 * q);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) put16(tid + 256 * q, val[q]);
+    } else {
+        for (int u = tid; u < 16 * vec_per_row; u += 256) put16(u, load16(u));
     }
     __syncthreads();
 
@@ -64,9 +80,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     }
     const int64_t chunk = ((int64_t)tile * G + g0 + gl) * 16 + i;
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-        *reinterpret_cast<uint4 *>(planes + p * plane_bytes + chunk * 16) =
-            make_uint4(out[p][0], out[p][1], out[p][2], out[p][3]);
+    for (int p = 0; p < 8; ++p) {
+        const u32x4_t v = {out[p][0], out[p][1], out[p][2], out[p][3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(planes + p * plane_bytes + chunk * 16));
+    }
 }
 
 // Unpack test hook: thread per (row, group) chunk; reads planes 0..R-1 only,
