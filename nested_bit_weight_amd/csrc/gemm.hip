@@ -382,18 +382,30 @@ __global__ __launch_bounds__(64) void gemm_reduce_kernel(const float *__restrict
     f32x16_t tot;
 #pragma unroll
     for (int v = 0; v < 16; ++v) tot[v] = 0.f;
-    for (int z = 0; z < S; ++z) {
-        float4 v[4];
+    // Four splits per round: their 16 loads are all in flight before the
+    // first add (clamped at the end, so the count is static), and the adds
+    // keep the order z = 0, 1, ..., S-1.
+    for (int z0 = 0; z0 < S; z0 += 4) {
+        float4 v[4][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            v[q] = *reinterpret_cast<const float4 *>(src + (size_t)z * ntiles * GEMM_TILE +
-                                                     gemm_part_offset(bb, q, tid));
+        for (int zz = 0; zz < 4; ++zz)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            tot[4 * q] += v[q].x;
-            tot[4 * q + 1] += v[q].y;
-            tot[4 * q + 2] += v[q].z;
-            tot[4 * q + 3] += v[q].w;
+            for (int q = 0; q < 4; ++q)
+                v[zz][q] = *reinterpret_cast<const float4 *>(
+                    src + (size_t)min(z0 + zz, S - 1) * ntiles * GEMM_TILE +
+                    gemm_part_offset(bb, q, tid));
+        // (a repeat past the last split adds zero: a select, not a branch,
+        // so the loads stay ahead of every add)
+#pragma unroll
+        for (int zz = 0; zz < 4; ++zz) {
+            const bool live = z0 + zz < S;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tot[4 * q] += live ? v[zz][q].x : 0.f;
+                tot[4 * q + 1] += live ? v[zz][q].y : 0.f;
+                tot[4 * q + 2] += live ? v[zz][q].z : 0.f;
+                tot[4 * q + 3] += live ? v[zz][q].w : 0.f;
+            }
         }
     }
     const int nrow = blockIdx.x * GEMM_BN + 32 * w + (lane & 31);
