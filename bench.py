@@ -24,8 +24,10 @@ read of the same plane bytes takes in one launch (nbw_stream_read, same rotation
 and timing: the floor a launch of that size cannot beat, well under the 8 TB/s
 peak for tens of MB); the 12 products as 3 grouped dispatches; batch 4
 and 16 on the same linears; batch 256 (TFLOP/s, r in 8, 4, 3, 2, activations
-with 1% outlier channels x10); the CPU oracle timed on this host on a bounded
-sample of the batch-1 step.
+with 1% outlier channels x10); batch 1 on the largest single linears (70B-shaped
+gate_up and down, Qwen3-8B-shaped gate_up: plane bytes worth >= 5 us at the HBM
+peak) with their read floors (``large_b1``); the CPU oracle timed on this host on a
+bounded sample of the batch-1 step.
 """
 from __future__ import annotations
 
@@ -545,10 +547,63 @@ def main():
                                             for (nm, r), d in sorted(d256.items())]}
         log(f"batch 256: {tflops:.1f} TFLOP/s; {n256} {ach256:.1f} TFLOP/s")
 
+        # ---- batch 1 on the largest single linears (70B-shaped gate_up and down at r = 3, 2;
+        # Qwen3-8B-shaped gate_up at r = 6, 4): the shapes whose plane bytes take >= 5 us at the
+        # 8 TB/s peak, so that launch latency does not dominate the HBM fraction.  Uniform
+        # random codes and U(0.001, 0.01) scales generated on the GPU (the kernels' work does
+        # not depend on the values); each shape rotates over its own parent copies (> 1.2 GB).
+        result["large_b1"] = large_shapes_b1(torch, nbw, gen)
+        for e in result["large_b1"]:
+            log(f"large b1 {e['linear']} r={e['r']}: {e['us']} us, {e['GBps']} GB/s, "
+                f"{e['frac_hbm']:.3f} of HBM peak, {e['frac_of_read_floor']:.3f} of the read floor")
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth)
 
     print(json.dumps(result), flush=True)
+
+
+LARGE_SHAPES = (("70b gate_up", 57344, 8192, (3, 2)), ("70b down", 8192, 28672, (3, 2)),
+                ("qwen3-8b gate_up", 24576, 4096, (6, 4)))
+
+
+def large_shapes_b1(torch, nbw, gen):
+    """Batch-1 product time, plane bytes per second, and the plain read of the same bytes,
+    per (shape, r) of LARGE_SHAPES; every launch reads its own parent copy."""
+    sink = nbw.stream_sink()
+    out = []
+    for name, n, k, rs in LARGE_SHAPES:
+        pb = nbw.plane_bytes(n, k)
+        copies = max(2, -(-1_200_000_000 // (8 * pb)) + 1)
+        codes = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        ws, ss = [], []
+        for _ in range(copies):
+            codes.random_(0, 256, generator=gen)
+            ws.append(nbw.pack_bitplanes(codes))
+            ss.append((torch.rand((n, k // 128), device="cuda", generator=gen) * 0.009 + 0.001)
+                      .to(torch.bfloat16))
+        del codes
+        x = torch.randn((1, k), device="cuda", generator=gen).to(torch.bfloat16)
+        y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        for r in rs:
+            calls = [nbw.QgemmCall(x, ws[c].slice_view(r), ss[c], r, out=y) for c in range(copies)]
+            g = capture(torch, lambda cl=calls: [c() for c in cl])
+            g.replay()
+            us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / copies
+            del g
+            bufs = [w.storage for w in ws]
+            gf = capture(torch, lambda bl=bufs: [nbw.stream_read(b, r * pb, sink) for b in bl])
+            gf.replay()
+            fus = event_time(torch, lambda i: gf.replay(), 3) * 1e3 / copies
+            del gf
+            gbs = r * pb / (us * 1e-6) / 1e9
+            out.append({"linear": name, "n": n, "k": k, "r": r, "us": round(us, 2),
+                        "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "read_floor_us": round(fus, 2), "frac_of_read_floor": round(fus / us, 4),
+                        "kernel": nbw.kernel_name(1, n, k, r)})
+        del ws, ss
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(synth):
