@@ -567,7 +567,7 @@ LARGE_SHAPES = (("70b gate_up", 57344, 8192, (3, 2)), ("70b down", 8192, 28672, 
                 ("qwen3-8b gate_up", 24576, 4096, (6, 4)))
 
 
-def large_shapes_b1(torch, nbw, gen):
+def large_shapes_b1(torch, nbw, gen, kernel="auto"):
     """Batch-1 product time, plane bytes per second, and the plain read of the same bytes,
     per (shape, r) of LARGE_SHAPES; every launch reads its own parent copy."""
     sink = nbw.stream_sink()
@@ -586,7 +586,8 @@ def large_shapes_b1(torch, nbw, gen):
         x = torch.randn((1, k), device="cuda", generator=gen).to(torch.bfloat16)
         y = torch.empty((1, n), dtype=torch.float32, device="cuda")
         for r in rs:
-            calls = [nbw.QgemmCall(x, ws[c].slice_view(r), ss[c], r, out=y) for c in range(copies)]
+            calls = [nbw.QgemmCall(x, ws[c].slice_view(r), ss[c], r, out=y, kernel=kernel)
+                     for c in range(copies)]
             g = capture(torch, lambda cl=calls: [c() for c in cl])
             g.replay()
             us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / copies
@@ -600,7 +601,7 @@ def large_shapes_b1(torch, nbw, gen):
             out.append({"linear": name, "n": n, "k": k, "r": r, "us": round(us, 2),
                         "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                         "read_floor_us": round(fus, 2), "frac_of_read_floor": round(fus / us, 4),
-                        "kernel": nbw.kernel_name(1, n, k, r)})
+                        "kernel": nbw.kernel_name(1, n, k, r, kernel)})
         del ws, ss
         torch.cuda.empty_cache()
     return out
