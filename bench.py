@@ -26,8 +26,10 @@ peak for tens of MB); the 12 products as 3 grouped dispatches; batch 4
 and 16 on the same linears; batch 256 (TFLOP/s, r in 8, 4, 3, 2, activations
 with 1% outlier channels x10); batch 1 on the largest single linears (70B-shaped
 gate_up and down, Qwen3-8B-shaped gate_up: plane bytes worth >= 5 us at the HBM
-peak) with their read floors (``large_b1``); the CPU oracle timed on this host on a
-bounded sample of the batch-1 step.
+peak) with their read floors (``large_b1``); dense bf16 torch.matmul (hipBLASLt) on
+the Llama linears at batch 1 and 256 with the sliced products' speedup over it
+(``dense_bf16``, context only); the CPU oracle timed on this host on a bounded sample
+of the batch-1 step.
 """
 from __future__ import annotations
 
@@ -553,6 +555,11 @@ def main():
         # random codes and U(0.001, 0.01) scales generated on the GPU (the kernels' work does
         # not depend on the values); each shape rotates over its own parent copies (> 1.2 GB).
         result["large_b1"] = large_shapes_b1(torch, nbw, gen)
+
+        # ---- context: dense bf16 torch.matmul (hipBLASLt) on the same linears, batch 1 and 256,
+        # and the sliced products' speedup over it (the pages' Figure 1 sets its kernels against a
+        # dense FP16 matmul); the weights rotate over copies past the 256 MB MALL as above
+        result["dense_bf16"] = dense_context(torch, layer, result, gen)
         for e in result["large_b1"]:
             log(f"large b1 {e['linear']} r={e['r']}: {e['us']} us, {e['GBps']} GB/s, "
                 f"{e['frac_hbm']:.3f} of HBM peak, {e['frac_of_read_floor']:.3f} of the read floor")
@@ -561,6 +568,39 @@ def main():
         result["cpu_baseline"] = cpu_baseline(synth)
 
     print(json.dumps(result), flush=True)
+
+
+def dense_context(torch, layer, result, gen):
+    """Dense bf16 Y = X . W^T per Llama-3.1-8B linear at batch 1 and 256 (torch.mm on contiguous
+    operands, W^T stored [k][n]), graph-replayed over weight copies; beside it the sliced products'
+    times from this run and the speedup over dense."""
+    ours = {}
+    for e in result["per_shape"]:
+        ours[(e["linear"], e["r"], 1)] = e["us"]
+    for e in result.get("batch256", {}).get("per_shape", []):
+        ours[(e["linear"], e["r"], 256)] = e["us"]
+    out = []
+    for L in layer.lin:
+        n, k = L["n"], L["k"]
+        copies = max(2, -(-1_200_000_000 // (2 * n * k)) + 1)
+        wts = [(torch.randn((k, n), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+               for _ in range(copies)]
+        for b in (1, 256):
+            x = torch.randn((b, k), device="cuda", generator=gen).to(torch.bfloat16)
+            y = torch.empty((b, n), dtype=torch.bfloat16, device="cuda")
+            g = capture(torch, lambda wl=wts, xx=x, yy=y: [torch.mm(xx, wt, out=yy) for wt in wl])
+            g.replay()
+            us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / copies
+            del g
+            e = {"linear": L["name"], "batch": b, "dense_us": round(us, 2),
+                 "dense_TFLOPs": round(2 * b * n * k / (us * 1e-6) / 1e12, 1)}
+            sp = {str(r): round(us / ours[(L["name"], r, b)], 2)
+                  for (nm, r, bb) in sorted(ours) if nm == L["name"] and bb == b}
+            e["speedup_of_sliced_by_r"] = sp
+            out.append(e)
+        del wts
+        torch.cuda.empty_cache()
+    return out
 
 
 LARGE_SHAPES = (("70b gate_up", 57344, 8192, (3, 2)), ("70b down", 8192, 28672, (3, 2)),
