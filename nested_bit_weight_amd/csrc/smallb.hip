@@ -40,7 +40,12 @@
 namespace nbw {
 
 constexpr int SMALLB_WAVES = 8;      // waves per workgroup
-constexpr int SMALLB_MAX_TILES = 16; // tiles per workgroup
+constexpr int SMALLB_MAX_TILES = 14; // tiles per workgroup
+// Activation transpose buffer per wave: 16 batch rows x 256 bytes (one group),
+// rows padded to 272 bytes so that both the row-wise writes and the
+// column-wise reads hit 16 distinct 16-byte bank groups per 16 lanes.
+constexpr int SMALLB_XROW = 272;
+constexpr int SMALLB_XBUF = 16 * SMALLB_XROW;
 constexpr int SMALLB_DEPTH = 2;      // steps of planes in flight per wave
 
 __device__ __forceinline__ float sb_bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -74,9 +79,10 @@ __device__ __forceinline__ void sb_quad_transpose(uint32_t &r0, uint32_t &r1, ui
     r3 = f[1];
 }
 
-// Dynamic LDS: fp32 [W][T][4][64] partial sums (tile t, output v of lane l).
+// Dynamic LDS: fp32 [W][T][4][64] partial sums (tile t, output v of lane l),
+// then one activation transpose buffer per wave.
 __host__ __device__ constexpr size_t smallb_lds_bytes(int waves, int slots) {
-    return (size_t)waves * slots * 4 * 64 * 4;
+    return (size_t)waves * slots * 4 * 64 * 4 + (size_t)waves * SMALLB_XBUF;
 }
 
 // grid: (ceil(tiles / tiles_per_wg), ceil(batch / 16)); block 64 * SMALLB_WAVES.
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     int n, int k, int tiles_total, int tiles_per_wg, float *__restrict__ y, int64_t ldy,
     int ybf16) {
-    extern __shared__ __align__(16) float red[];  // [W][tiles_per_wg][4][64]
+    extern __shared__ __align__(16) float red[];  // [W][tiles_per_wg][4][64], then [W] x buffers
     constexpr int NPH = Phases<R>::count;
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
@@ -98,13 +104,12 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     const int c = lane & 15, d = lane >> 4;
     const int t_begin = blockIdx.x * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    const int64_t bcol = (int64_t)blockIdx.y * 16 + c;
-    const bool bvalid = bcol < batch;
-    const int64_t bclamp = bvalid ? bcol : batch - 1;
+    const int64_t b0 = (int64_t)blockIdx.y * 16;
 
     // This wave's sets: ordinal s = 0 .. my_sets-1 is set w + s*W.
     const int my_sets = nsets > w ? (nsets - w + W - 1) / W : 0;
     float *slot = red + (size_t)w * tiles_per_wg * 256;
+    uint8_t *xbuf = reinterpret_cast<uint8_t *>(red + (size_t)W * tiles_per_wg * 256) + w * SMALLB_XBUF;
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) slot[(t * 4 + v) * 64 + lane] = 0.f;
@@ -136,8 +141,10 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
                 uint32_t h[4], hz[4];
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi) {
+                    // a group past k gets scale 0: its activations are a
+                    // repeat of the last group's, not zeros
                     const int64_t idx = (int64_t)row * G + min(4 * set + gi, G - 1);
-                    h[gi] = scales[idx];
+                    h[gi] = 4 * set + gi < G ? scales[idx] : 0u;
                     if constexpr (ASYM) hz[gi] = zeros[idx];
                 }
                 sw[j][v][0] = h[0] | (h[1] << 16);
@@ -166,26 +173,58 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     };
 
     // Activation operands of the current set: XB[gi][4j+e] is the bf16 pair of
-    // columns 128g + 32d + 8j + 2e (+1) of batch row bcol; the chains'
+    // columns 128g + 32d + 8j + 2e (+1) of batch row b0 + c; the chains'
     // starting values (corrections) and the group sums of X.
+    //
+    // The lane needs 64 contiguous bytes of its row per group, but loading
+    // them directly puts a wave's 16-byte pieces 64 bytes apart: each
+    // instruction then touches 32 cache lines and uses a quarter of each, and
+    // the activation loads cost more than the planes.  Instead instruction j
+    // of group gi reads 16-byte piece l%16 of batch row 4j + l/16 (four whole
+    // rows of the group, 8 full lines), and the wave transposes the pieces
+    // through its LDS buffer when the set starts (xstage).
+    // (Unconditional loads: batch rows past the end repeat the last row and
+    // are never stored; groups past k repeat the last group and have scale 0.
+    // A load under a lane condition made the compiler wait for the
+    // activations before issuing the plane loads.)
     uint32_t XB[4][16];
     float init[4], xsum[4];
-    auto load_set = [&](int set) {
+    auto load_x = [&](int set) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-            const int g = 4 * set + gi;
-            const bool ok = bvalid && g < G;
-            const int gc = g < G ? g : G - 1;
-            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + bclamp * ldx + 128 * gc + 32 * d);
+            const int gc = min(4 * set + gi, G - 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const u32x4_t v = ok ? src[j] : u32x4_t{0u, 0u, 0u, 0u};
+                const int64_t row = min(b0 + 4 * j + d, batch - 1);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(x + row * ldx + 128 * gc + 8 * c);
                 XB[gi][4 * j] = v.x;
                 XB[gi][4 * j + 1] = v.y;
                 XB[gi][4 * j + 2] = v.z;
                 XB[gi][4 * j + 3] = v.w;
             }
         }
+    };
+    // XB[gi][4j..4j+3] holds piece c of row 4j + d; afterwards piece 4d + j of
+    // row c.  (In-order LDS access within a wave: no barrier.)
+    auto xstage = [&]() {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<u32x4_t *>(xbuf + (4 * j + d) * SMALLB_XROW + 16 * c) =
+                    u32x4_t{XB[gi][4 * j], XB[gi][4 * j + 1], XB[gi][4 * j + 2], XB[gi][4 * j + 3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xbuf + c * SMALLB_XROW + 16 * (4 * d + j));
+                XB[gi][4 * j] = v.x;
+                XB[gi][4 * j + 1] = v.y;
+                XB[gi][4 * j + 2] = v.z;
+                XB[gi][4 * j + 3] = v.w;
+            }
+        }
+    };
+    auto make_init = [&]() {
+        xstage();
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             init[gi] = sb_cross_row_sum(correction<R, 16>(XB[gi]));
@@ -224,9 +263,8 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
                                                                 __builtin_bit_cast(bf16x8_t, xb), P, 0, 0, 0);
                 }
             }
-            // This lane holds rows 4d..4d+3 of the tile for batch row bcol.
-            // (No guard on the scale: a group past k has zero activations, so
-            // its chain is zero, and rows past n are never stored.)
+            // This lane holds rows 4d..4d+3 of the tile for batch row b0 + c.
+            // (A group past k has scale 0; rows past n are never stored.)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const uint32_t word = sw[j][v][gi >> 1];
@@ -258,33 +296,64 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         }
     };
 
-    for (int si = 0; si < my_sets; ++si) {
-        const int set = w + si * W;
-        // The set's activations first (staging them waits for nothing else:
-        // a set starts with no loads in flight), then the first PD tiles.
-        load_set(set);
+    // The wave's steps are (set ordinal si, tile t), set-major.  Loads run PD
+    // steps ahead across set boundaries (past the last step they repeat it);
+    // a new set's activations are loaded when its first step comes up.
+    const int nsteps = my_sets * T;
+    int lsi = 0, lt = 0;  // the next step to load
+    auto load_next = [&](int j) {
+        const bool past = lsi >= my_sets;
+        load_step(j, w + (past ? my_sets - 1 : lsi) * W, past ? T - 1 : lt);
+        if (++lt == T) {
+            lt = 0;
+            ++lsi;
+        }
+    };
+    if (nsteps > 0) {
+        load_x(w);
 #pragma unroll
         for (int j = 0; j < PD; ++j) {
             // (in order: the loads in flight at the loop top then match the
             // steady state, and the waits there stay partial)
             __builtin_amdgcn_sched_barrier(0);
-            load_step(j, set, j);
+            load_next(j);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const int Tfull = T / PD * PD;
-        for (int t0 = 0; t0 < Tfull; t0 += PD) {
+        make_init();  // (waits for the activations only: they were issued first)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int csi = 0, ct = 0;  // the step being computed
+    const int nfull = nsteps / PD * PD;
+    for (int i0 = 0; i0 < nfull; i0 += PD) {
 #pragma unroll
-            for (int j = 0; j < PD; ++j) {
-                const f32x4_t v4 = compute(j);
-                load_step(j, set, t0 + j + PD);  // refill as soon as the buffer is free
-                commit(si, t0 + j, v4);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < PD; ++j) {
+            if (ct == 0 && csi > 0) {
+                load_x(w + csi * W);
+                make_init();
+            }
+            const f32x4_t v4 = compute(j);
+            load_next(j);  // refill as soon as the buffer is free
+            commit(csi, ct, v4);
+            if (++ct == T) {
+                ct = 0;
+                ++csi;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PD; ++j)  // the last < PD steps are already loaded
+        if (nfull + j < nsteps) {
+            if (ct == 0 && csi > 0) {
+                load_x(w + csi * W);
+                make_init();
+            }
+            commit(csi, ct, compute(j));
+            if (++ct == T) {
+                ct = 0;
+                ++csi;
             }
         }
-#pragma unroll
-        for (int j = 0; j < PD; ++j)  // the last < PD tiles are already loaded
-            if (Tfull + j < T) commit(si, Tfull + j, compute(j));
-    }
 
     // Outputs: add the waves' slots in a fixed order.
     __syncthreads();
