@@ -7,12 +7,14 @@
 // the plane decode itself, so the contraction moves to the matrix cores; the
 // product is still bound by HBM, so the kernel streams like the batch-1 one:
 //
-//  - one v_mfma_f32_16x16x32_bf16 multiplies a 16-row x 32-column weight
-//    fragment by 32 columns of up to 16 batch rows.  Lane l supplies row l%16,
-//    k-quarter l/16 of the weight fragment, and batch row l%16, k-quarter l/16
-//    of the activations; the k-slot order inside a quarter only has to agree
-//    between the two operands, so each lane feeds its decoded plane word in
-//    the order the decoder produces it (pairs 4j..4j+3 -> MFMA j).
+//  - one v_mfma_f32_16x16x32_bf16 multiplies 32 columns of up to 16 batch
+//    rows (A operand) by a 32-column x 16-row weight fragment (B operand).
+//    Lane l supplies batch row l%16, k-quarter l/16 of the activations and
+//    weight row l%16, k-quarter l/16 of the weights, and ends holding batch
+//    rows 4(l/16)..4(l/16)+3 of weight row l%16: one scale per lane and
+//    group.  The k-slot order inside a quarter only has to agree between the
+//    two operands, so each lane feeds its decoded plane word in the order the
+//    decoder produces it (pairs 4j..4j+3 -> MFMA j).
 //  - lane (row c, quarter d) of a wave loads the whole 16-byte chunk of row c
 //    of group 4*set + d for each plane (one wave load covers the 1 KB of a
 //    16-row tile's four groups), and a 4 x 4 transpose across the quarter
@@ -22,16 +24,17 @@
 //    addresser's time went with the count of instructions, not of bytes.)
 //  - a workgroup owns a run of T 16-row tiles and all of k (about one
 //    workgroup per CU); its waves split k into 4-group sets (wave w: sets w,
-//    w+W, ...).  For each of its sets a wave loads the set's activation
-//    operands (16 batch rows x 512 columns, 64 registers per lane), then
-//    walks the T tiles with PD tiles of planes and scales in flight.  The
-//    loads inside a set are unconditional (clamped at the end), so the loads
-//    in flight between a load and its use are a static count.
+//    w+W, ...).  A wave's steps are (set, tile) pairs, set-major: when a set
+//    starts, the wave loads its activation operands (16 batch rows x 512
+//    columns, 64 registers per lane), and the planes and scales run PD steps
+//    ahead across set boundaries.  Loads are unconditional (clamped at the
+//    end), so the loads in flight between a load and its use are a static
+//    count.
 //  - every MFMA chain covers one 128-wide group and starts from the
 //    correction that removes the decoded operands' constant offsets; the
 //    group scale is folded in fp32 right after it (one FMA per output).
 //  - each lane adds its four outputs of a step to its own LDS slot for the
-//    tile (an add that returns nothing); the waves meet there at the end.
+//    tile; the waves meet there at the end.
 #include <cstdio>
 
 #include "decode.h"
@@ -114,67 +117,62 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) slot[(t * 4 + v) * 64 + lane] = 0.f;
 
-    // Step loads: the lane's 16-byte plane chunks (group 4*set + d);
-    // for each of the lane's 4 output rows (4d + v), the scales (and zero
-    // points) of the 4 groups.
+    // Step loads: the lane's 16-byte plane chunks (row c, group 4*set + d)
+    // and the scales (and zero points) of its output row c for the set's 4
+    // groups.  Addresses are a wave-uniform base plus a per-lane 32-bit
+    // offset, so the loads take a scalar base and no 64-bit vector adds.
     uint32_t pl[PD][4][R];
-    uint32_t sw[PD][4][2];
-    uint32_t zw[ASYM ? PD : 1][4][2];
+    uint32_t sw[PD][2];
+    uint32_t zw[ASYM ? PD : 1][2];
     auto load_step = [&](int j, int set, int t) {
         const int tile = t_begin + min(t, T - 1);
         // (scales first: loads retire in issue order, and the plane words,
         // used first, should not be the last ones issued)
+        const uint32_t srow = (uint32_t)min(c, n - 1 - 16 * tile) * (uint32_t)G;
+        const int64_t sbase = (int64_t)16 * tile * G + 4 * set;
+        if constexpr (S4) {
+            const uint2 sv = *reinterpret_cast<const uint2 *>(scales + sbase + srow);
+            sw[j][0] = sv.x;
+            sw[j][1] = sv.y;
+            if constexpr (ASYM) {
+                const uint2 zv = *reinterpret_cast<const uint2 *>(zeros + sbase + srow);
+                zw[j][0] = zv.x;
+                zw[j][1] = zv.y;
+            }
+        } else {
+            uint32_t h[4], hz[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int row = min(16 * tile + 4 * d + v, n - 1);
-            if constexpr (S4) {
-                const int64_t idx = (int64_t)row * G + 4 * set;  // (4-aligned: G % 4 == 0)
-                const uint2 sv = *reinterpret_cast<const uint2 *>(scales + idx);
-                sw[j][v][0] = sv.x;
-                sw[j][v][1] = sv.y;
-                if constexpr (ASYM) {
-                    const uint2 zv = *reinterpret_cast<const uint2 *>(zeros + idx);
-                    zw[j][v][0] = zv.x;
-                    zw[j][v][1] = zv.y;
-                }
-            } else {
-                uint32_t h[4], hz[4];
-#pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
-                    // a group past k gets scale 0: its activations are a
-                    // repeat of the last group's, not zeros
-                    const int64_t idx = (int64_t)row * G + min(4 * set + gi, G - 1);
-                    h[gi] = 4 * set + gi < G ? scales[idx] : 0u;
-                    if constexpr (ASYM) hz[gi] = zeros[idx];
-                }
-                sw[j][v][0] = h[0] | (h[1] << 16);
-                sw[j][v][1] = h[2] | (h[3] << 16);
-                if constexpr (ASYM) {
-                    zw[j][v][0] = hz[0] | (hz[1] << 16);
-                    zw[j][v][1] = hz[2] | (hz[3] << 16);
-                }
+            for (int gi = 0; gi < 4; ++gi) {
+                // a group past k gets scale 0: its activations are a repeat
+                // of the last group's, not zeros
+                const int64_t gb = (int64_t)16 * tile * G + min(4 * set + gi, G - 1);
+                h[gi] = 4 * set + gi < G ? scales[gb + srow] : 0u;
+                if constexpr (ASYM) hz[gi] = zeros[gb + srow];
+            }
+            sw[j][0] = h[0] | (h[1] << 16);
+            sw[j][1] = h[2] | (h[3] << 16);
+            if constexpr (ASYM) {
+                zw[j][0] = hz[0] | (hz[1] << 16);
+                zw[j][1] = hz[2] | (hz[3] << 16);
             }
         }
         // row c's chunk of group 4*set + d, words q = 0..3 in pl[j][q][p]
         // (transposed across the quarter lanes just before the decode)
-        {
-            const int g = min(4 * set + d, G - 1);
-            const uint8_t *base = planes + (((int64_t)tile * G + g) * 16 + c) * 16;
+        const uint8_t *pbase = planes + ((int64_t)tile * G + 4 * set) * 256;
+        const uint32_t poff = (uint32_t)(S4 ? d : min(d, G - 1 - 4 * set)) * 256u + 16u * (uint32_t)c;
 #pragma unroll
-            for (int p = 0; p < R; ++p) {
-                const u32x4_t v = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t *>(base + p * plane_bytes));
-                pl[j][0][p] = v.x;
-                pl[j][1][p] = v.y;
-                pl[j][2][p] = v.z;
-                pl[j][3][p] = v.w;
-            }
+        for (int p = 0; p < R; ++p) {
+            const u32x4_t v =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(pbase + p * plane_bytes + poff));
+            pl[j][0][p] = v.x;
+            pl[j][1][p] = v.y;
+            pl[j][2][p] = v.z;
+            pl[j][3][p] = v.w;
         }
     };
 
     // Activation operands of the current set: XB[gi][4j+e] is the bf16 pair of
-    // columns 128g + 32d + 8j + 2e (+1) of batch row b0 + c; the chains'
-    // starting values (corrections) and the group sums of X.
+    // columns 128g + 32d + 8j + 2e (+1) of batch row b0 + c.
     //
     // The lane needs 64 contiguous bytes of its row per group, but loading
     // them directly puts a wave's 16-byte pieces 64 bytes apart: each
@@ -188,15 +186,15 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     // A load under a lane condition made the compiler wait for the
     // activations before issuing the plane loads.)
     uint32_t XB[4][16];
-    float init[4], xsum[4];
     auto load_x = [&](int set) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const int gc = min(4 * set + gi, G - 1);
+            const uint16_t *xg = x + b0 * ldx + 128 * gc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t row = min(b0 + 4 * j + d, batch - 1);
-                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(x + row * ldx + 128 * gc + 8 * c);
+                const int64_t row = min((int64_t)(4 * j + d), batch - 1 - b0);
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xg + row * ldx + 8 * c);
                 XB[gi][4 * j] = v.x;
                 XB[gi][4 * j + 1] = v.y;
                 XB[gi][4 * j + 2] = v.z;
@@ -223,20 +221,40 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
             }
         }
     };
+    // The chains' starting values: the correction of batch row 4d + v for
+    // group gi (init4[gi][v]), and for zero points the group sums of X
+    // (xsum4[gi][v]).  Each is formed in the lanes of its own batch row (row
+    // c), then moved to the lanes that hold that batch row's outputs through
+    // the LDS buffer.
+    f32x4_t init4[4], xsum4[ASYM ? 4 : 1];
     auto make_init = [&]() {
         xstage();
+        float cr[4], sx[4];
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-            init[gi] = sb_cross_row_sum(correction<R, 16>(XB[gi]));
+            cr[gi] = sb_cross_row_sum(correction<R, 16>(XB[gi]));
             if constexpr (ASYM) {
                 const uint32_t one = 0x3F803F80u;
-                float sx = 0.f;
+                float a = 0.f;
 #pragma unroll
                 for (int m = 0; m < 16; ++m)
-                    sx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
-                                                         __builtin_bit_cast(bf16x2_t, XB[gi][m]), sx,
-                                                         false);
-                xsum[gi] = sb_cross_row_sum(sx);
+                    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
+                                                        __builtin_bit_cast(bf16x2_t, XB[gi][m]), a, false);
+                sx[gi] = sb_cross_row_sum(a);
+            }
+        }
+        // (every quarter lane of row c writes the same values)
+        *reinterpret_cast<f32x4_t *>(xbuf + 16 * c) = f32x4_t{cr[0], cr[1], cr[2], cr[3]};
+        if constexpr (ASYM) *reinterpret_cast<f32x4_t *>(xbuf + 256 + 16 * c) = f32x4_t{sx[0], sx[1], sx[2], sx[3]};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const f32x4_t q = *reinterpret_cast<const f32x4_t *>(xbuf + 16 * (4 * d + v));
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) init4[gi][v] = q[gi];
+            if constexpr (ASYM) {
+                const f32x4_t u = *reinterpret_cast<const f32x4_t *>(xbuf + 256 + 16 * (4 * d + v));
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi) xsum4[gi][v] = u[gi];
             }
         }
     };
@@ -250,41 +268,42 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         for (int gi = 0; gi < 4; ++gi) {
             uint32_t D0[16], D1[16];
             decode_word<R>(pl[j][gi], D0, D1);
-            f32x4_t P = {init[gi], init[gi], init[gi], init[gi]};
+            // activations are the A operand (rows: batch), weights the B
+            // operand (columns: weight rows): lane (c, d) ends with batch rows
+            // 4d..4d+3 of weight row c
+            f32x4_t P = init4[gi];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const u32x4_t xb = {XB[gi][4 * jj], XB[gi][4 * jj + 1], XB[gi][4 * jj + 2], XB[gi][4 * jj + 3]};
                 const u32x4_t a0 = {D0[4 * jj], D0[4 * jj + 1], D0[4 * jj + 2], D0[4 * jj + 3]};
-                P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
-                                                            __builtin_bit_cast(bf16x8_t, xb), P, 0, 0, 0);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb),
+                                                            __builtin_bit_cast(bf16x8_t, a0), P, 0, 0, 0);
                 if constexpr (NPH == 2) {
                     const u32x4_t a1 = {D1[4 * jj], D1[4 * jj + 1], D1[4 * jj + 2], D1[4 * jj + 3]};
-                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1),
-                                                                __builtin_bit_cast(bf16x8_t, xb), P, 0, 0, 0);
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb),
+                                                                __builtin_bit_cast(bf16x8_t, a1), P, 0, 0, 0);
                 }
             }
-            // This lane holds rows 4d..4d+3 of the tile for batch row b0 + c.
             // (A group past k has scale 0; rows past n are never stored.)
+            const uint32_t word = sw[j][gi >> 1];
+            const float s = sb_bf16_to_f32((gi & 1) ? (word >> 16) : (word & 0xFFFFu));
+            if constexpr (ASYM) {  // + (127.5 - z) * 2^(R-8) * sum of the group's X
+                const uint32_t zword = zw[j][gi >> 1];
+                const float z = sb_bf16_to_f32((gi & 1) ? (zword >> 16) : (zword & 0xFFFFu));
+                const float zc = (127.5f - z) * (1.0f / (float)(1 << (8 - R)));
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t word = sw[j][v][gi >> 1];
-                const float s = sb_bf16_to_f32((gi & 1) ? (word >> 16) : (word & 0xFFFFu));
-                float pv = P[v];
-                if constexpr (ASYM) {  // + (127.5 - z) * 2^(R-8) * sum of the group's X
-                    const uint32_t zword = zw[j][v][gi >> 1];
-                    const float z = sb_bf16_to_f32((gi & 1) ? (zword >> 16) : (zword & 0xFFFFu));
-                    pv = fmaf((127.5f - z) * (1.0f / (float)(1 << (8 - R))), xsum[gi], pv);
-                }
-                out[v] = fmaf(s, pv, out[v]);
+                for (int v = 0; v < 4; ++v) P[v] = fmaf(zc, xsum4[gi][v], P[v]);
             }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[v] = fmaf(s, P[v], out[v]);
         }
         return out;
     };
-    // Add a tile's four outputs to this lane's slot.  One writer per slot (this
-    // lane), so no atomic is needed and the order of the additions is fixed:
-    // the wave's first set stores, later sets read, add and store.  (LDS float
-    // atomics serialize across the CU: four wave-wide ds_add_f32 per step
-    // doubled the kernel's time.)
+    // Add a step's four outputs to this lane's slot for the tile.  One writer
+    // per slot (this lane), so no atomic is needed and the order of the
+    // additions is fixed: the wave's first set stores, later sets read, add
+    // and store.  (LDS float atomics serialize across the CU: four wave-wide
+    // ds_add_f32 per step doubled the kernel's time.)
     auto commit = [&](int si, int t, const f32x4_t &v4) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -362,8 +381,8 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
         float sum = 0.f;
         for (int ww = 0; ww < W; ++ww) sum += red[((size_t)ww * tiles_per_wg + t) * 256 + v * 64 + l];
-        const int row = 16 * (t_begin + t) + 4 * (l >> 4) + v;
-        const int64_t b = (int64_t)blockIdx.y * 16 + (l & 15);
+        const int row = 16 * (t_begin + t) + (l & 15);
+        const int64_t b = b0 + 4 * (l >> 4) + v;
         if (row < n && b < batch) store_y(y, ybf16, b * ldy + row, sum * post);
     }
 }
