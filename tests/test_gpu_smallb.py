@@ -1,0 +1,79 @@
+"""GPU parity of the small-batch kernel where its step order crosses set boundaries.
+
+The kernel walks (set, tile) steps set-major and prefetches planes and scales
+across set boundaries; a workgroup holds a run of tiles and each wave several
+sets.  These shapes make every boundary case meet in one launch:
+
+* n = 6149: 385 tiles, two per workgroup, the last tile ragged (rows past n);
+* k = 4224: 33 groups, so k/128 is not a multiple of 4 and the last set holds
+  one group (the three groups past k carry scale 0 and repeated activations);
+  9 sets over 8 waves, so wave 0 runs two sets;
+* batch 7 (rows past the batch in the MFMA tile) and 16, r = 3 and 5 (one and
+  two decode phases), plus zero points.
+
+Every output is compared with the fp64 oracle.  Bars as in test_gpu_parity.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT = 2e-3
+DESIGN_BOUND = 1e-4
+N, K = 6149, 4224
+
+
+@pytest.fixture(scope="module")
+def nbw():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import nested_bit_weight_amd as m
+    m.library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def case():
+    return synth.random_case(N, K, 16, seed=77, recipe="gptq_like", outliers=True)
+
+
+def rel_err(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    return float((np.abs(y - ref).max(axis=1) / den).max())
+
+
+@pytest.mark.parametrize("batch", [7, 16])
+@pytest.mark.parametrize("r", [3, 5])
+def test_smallb_set_boundaries_every_output(nbw, case, batch, r):
+    print(f"smallb n={N} k={K} batch={batch} r={r}", flush=True)
+    assert nbw.kernel_name(batch, N, K, r).startswith("nbw::smallb_kernel")
+    w = nbw.pack_bitplanes(torch.from_numpy(case["codes"]).cuda())
+    xb = np.ascontiguousarray(case["x"][:batch])
+    x = torch.from_numpy(xb).view(torch.bfloat16).cuda()
+    s = torch.from_numpy(case["scales"]).view(torch.bfloat16).cuda()
+    y = nbw.qgemm(x, w.slice_view(r), s, r).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    e = rel_err(y, oracle.qgemm(xb, oracle.pack(case["codes"]), case["scales"], N, K, r))
+    print(f"  err={e:.3e}", flush=True)
+    assert e <= CONTRACT and e <= DESIGN_BOUND
+
+
+def test_smallb_set_boundaries_asym(nbw, case):
+    batch, r = 9, 4
+    print(f"smallb asym n={N} k={K} batch={batch} r={r}", flush=True)
+    rng = np.random.default_rng(78)
+    z = synth.f32_to_bf16_bits(rng.integers(96, 160, size=(N, K // 128)).astype(np.float32))
+    w = nbw.pack_bitplanes(torch.from_numpy(case["codes"]).cuda())
+    xb = np.ascontiguousarray(case["x"][:batch])
+    x = torch.from_numpy(xb).view(torch.bfloat16).cuda()
+    s = torch.from_numpy(case["scales"]).view(torch.bfloat16).cuda()
+    zd = torch.from_numpy(z).view(torch.bfloat16).cuda()
+    y = nbw.qgemm(x, w.slice_view(r), s, r, zeros=zd).cpu().numpy()
+    ref = oracle.qgemm_asym(xb, oracle.pack(case["codes"]), case["scales"], z, N, K, r)
+    e = rel_err(y, ref)
+    print(f"  err={e:.3e}", flush=True)
+    assert e <= CONTRACT and e <= DESIGN_BOUND
