@@ -83,11 +83,15 @@ typedef struct nbw_wview {
     int64_t plane_bytes; /* ceil(n/16)*16*k/8 */
 } nbw_wview;
 
-/* Kernel selectors for nbw_qgemm_kernel (NBW_KERNEL_AUTO picks by batch). */
+/* Kernel selectors for nbw_qgemm_kernel.  NBW_KERNEL_AUTO picks by batch:
+ * 1 -> GEMV; otherwise SMALLB while it needs one pass over the planes, or
+ * two passes and k <= 8192 (a pass covers 32 batch rows for r <= 4 when the
+ * workgroups' tile runs are short, else 16); otherwise GEMM.  Batches 2..16
+ * always take SMALLB and batches above 64 always GEMM. */
 typedef enum nbw_kernel {
     NBW_KERNEL_AUTO = 0,
     NBW_KERNEL_GEMV = 1,   /* VALU dequant + bf16 dot2, batch 1..2 per launch slice */
-    NBW_KERNEL_SMALLB = 2, /* in-register dequant feeding MFMA, 16 batch rows per slice */
+    NBW_KERNEL_SMALLB = 2, /* in-register dequant feeding MFMA, 16 or 32 batch rows per pass */
     NBW_KERNEL_GEMM = 3    /* large-batch MFMA kernel */
 } nbw_kernel;
 

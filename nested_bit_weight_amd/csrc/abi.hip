@@ -54,6 +54,31 @@ nbw_status check_view(const nbw_wview *w) {
     return NBW_OK;
 }
 
+// NBW_KERNEL_AUTO: batch 1 -> GEMV.  Otherwise the small-batch kernel while
+// it needs at most two passes over the planes (16 or 32 batch rows a pass)
+// and, for two, k <= 8192; else the large-batch GEMM, which reads the planes
+// about once at any batch.  (Measured on the Llama-3.1-8B linears at r = 2..8:
+// two passes beat the GEMM except on down, k = 14336, where every workgroup
+// reads the whole of X each pass; four passes lose.)  Batches up to 16 and
+// above 64 need no device query.
+nbw_status auto_kernel(int64_t batch, int64_t n, int64_t k, int32_t r, int *kernel) {
+    if (batch <= 1) {
+        *kernel = NBW_KERNEL_GEMV;
+        return NBW_OK;
+    }
+    if (batch <= 16 || batch > 64) {
+        *kernel = batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM;
+        return NBW_OK;
+    }
+    int cus = 0;
+    const nbw_status st = cu_count(&cus);
+    if (st != NBW_OK) return st;
+    const int64_t rows = nbw::smallb_pass_rows(r, (int)n, cus);
+    const int64_t passes = (batch + rows - 1) / rows;
+    *kernel = passes == 1 || (passes == 2 && k <= 8192) ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM;
+    return NBW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,8 +156,10 @@ nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
     st = cu_count(&cus);
     if (st != NBW_OK) return st;
     int kernel = o.kernel;
-    if (kernel == NBW_KERNEL_AUTO)
-        kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
+    if (kernel == NBW_KERNEL_AUTO) {
+        st = auto_kernel(batch, w->n, w->k, r, &kernel);
+        if (st != NBW_OK) return st;
+    }
     nbw::QgemmArgs a;
     a.x = (const uint16_t *)x_bf16;
     a.batch = batch;
@@ -259,9 +286,9 @@ int64_t nbw_qgemm_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t r
         kernel > NBW_KERNEL_GEMM)
         return -1;
     if (batch == 0) return 0;
-    if (kernel == NBW_KERNEL_AUTO)
-        kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
-    if (kernel != NBW_KERNEL_GEMM) return 0;
+    int kn = kernel;
+    if (kn == NBW_KERNEL_AUTO && auto_kernel(batch, n, k, r, &kn) != NBW_OK) return -1;
+    if (kn != NBW_KERNEL_GEMM) return 0;
     int cus = 0;
     if (cu_count(&cus) != NBW_OK) return -1;
     nbw::QgemmArgs a = {};
@@ -287,13 +314,13 @@ const char *nbw_kernel_name(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_
         return "";
     int cus = 0;
     if (cu_count(&cus) != NBW_OK) return "";
-    if (kernel == NBW_KERNEL_AUTO)
-        kernel = batch == 1 ? NBW_KERNEL_GEMV : (batch <= 16 ? NBW_KERNEL_SMALLB : NBW_KERNEL_GEMM);
+    int kn = kernel;
+    if (kn == NBW_KERNEL_AUTO && auto_kernel(batch, n, k, r, &kn) != NBW_OK) return "";
     nbw::QgemmArgs a = {};
     a.batch = batch;
     a.n = (int)n;
     a.k = (int)k;
-    switch (kernel) {
+    switch (kn) {
     case NBW_KERNEL_GEMV: nbw::gemv_name(r, a, cus, buf, sizeof buf); break;
     case NBW_KERNEL_SMALLB: nbw::smallb_name(r, a, cus, buf, sizeof buf); break;
     default: nbw::gemm_name(r, a, cus, buf, sizeof buf); break;

@@ -50,6 +50,8 @@ hipError_t launch_unpack(int r, const uint8_t *planes, int64_t plane_bytes, int 
                          uint8_t *codes, hipStream_t stream);
 hipError_t launch_gemv(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
+// Batch rows the small-batch kernel covers per pass over the planes (16 or 32).
+int smallb_pass_rows(int r, int n, int cu_count);
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
 // Workspace bytes the large-batch GEMM uses to split k deterministically (0:
 // the launch does not split).

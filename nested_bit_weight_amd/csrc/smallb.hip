@@ -30,9 +30,11 @@
 //    ahead across set boundaries.  Loads are unconditional (clamped at the
 //    end), so the loads in flight between a load and its use are a static
 //    count.
-//  - every MFMA chain covers one 128-wide group and starts from the
-//    correction that removes the decoded operands' constant offsets; the
-//    group scale is folded in fp32 right after it (one FMA per output).
+//  - every MFMA chain covers one 128-wide group and starts from zero; the
+//    group scale is folded in fp32 right after it (one FMA per output), and
+//    the corrections that remove the decoded operands' constant offsets
+//    enter through one fp32 MFMA per step (corrections x scales over the
+//    set's four groups).
 //  - each lane adds its four outputs of a step to its own LDS slot for the
 //    tile; the waves meet there at the end.
 #include <cstdio>
@@ -82,22 +84,29 @@ __device__ __forceinline__ void sb_quad_transpose(uint32_t &r0, uint32_t &r1, ui
     r3 = f[1];
 }
 
-// Dynamic LDS: fp32 [W][T][4][64] partial sums (tile t, output v of lane l),
-// then one activation transpose buffer per wave.
-__host__ __device__ constexpr size_t smallb_lds_bytes(int waves, int slots) {
-    return (size_t)waves * slots * 4 * 64 * 4 + (size_t)waves * SMALLB_XBUF;
+// Dynamic LDS: fp32 [W][T][NB][4][64] partial sums (tile t, batch slice s,
+// output v of lane l), then one activation transpose buffer per wave.
+__host__ __device__ constexpr size_t smallb_lds_bytes(int waves, int slots, int nb) {
+    return (size_t)waves * slots * nb * 4 * 64 * 4 + (size_t)waves * SMALLB_XBUF;
 }
+// Two 16-row batch slices per workgroup (32 batch rows per pass over the
+// planes) for r <= 4 without zero points, when the tile run is at most this
+// long (LDS: 2 KB of partial sums per wave and tile).
+constexpr int SMALLB_NB2_MAX_TILES = 7;
 
-// grid: (ceil(tiles / tiles_per_wg), ceil(batch / 16)); block 64 * SMALLB_WAVES.
+// grid: (ceil(tiles / tiles_per_wg), ceil(batch / (16 NB))); block 64 * SMALLB_WAVES.
 // S4: k/128 is a multiple of 4, so the scales (and zero points) of a row's
 // four groups of a set are one aligned 8-byte word.
-template <int R, int PD, bool ASYM, bool S4>
+// NB: 16-row batch slices per workgroup.  Each decoded weight fragment feeds
+// the MFMAs of every slice, so the plane decode, the dominant cost, is paid
+// once per NB slices.
+template <int R, int PD, bool ASYM, bool S4, int NB>
 __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     const uint16_t *__restrict__ x, int64_t batch, int64_t ldx, const uint8_t *__restrict__ planes,
     int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     int n, int k, int tiles_total, int tiles_per_wg, float *__restrict__ y, int64_t ldy,
     int ybf16) {
-    extern __shared__ __align__(16) float red[];  // [W][tiles_per_wg][4][64], then [W] x buffers
+    extern __shared__ __align__(16) float red[];  // [W][tiles_per_wg][NB][4][64], then [W] x buffers
     constexpr int NPH = Phases<R>::count;
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
@@ -107,15 +116,15 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     const int c = lane & 15, d = lane >> 4;
     const int t_begin = blockIdx.x * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    const int64_t b0 = (int64_t)blockIdx.y * 16;
+    const int64_t b0 = (int64_t)blockIdx.y * 16 * NB;
 
     // This wave's sets: ordinal s = 0 .. my_sets-1 is set w + s*W.
     const int my_sets = nsets > w ? (nsets - w + W - 1) / W : 0;
-    float *slot = red + (size_t)w * tiles_per_wg * 256;
-    uint8_t *xbuf = reinterpret_cast<uint8_t *>(red + (size_t)W * tiles_per_wg * 256) + w * SMALLB_XBUF;
+    float *slot = red + (size_t)w * tiles_per_wg * 256 * NB;
+    uint8_t *xbuf = reinterpret_cast<uint8_t *>(red + (size_t)W * tiles_per_wg * 256 * NB) + w * SMALLB_XBUF;
     for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) slot[(t * 4 + v) * 64 + lane] = 0.f;
+        for (int q = 0; q < 4 * NB; ++q) slot[(t * 4 * NB + q) * 64 + lane] = 0.f;
 
     // Step loads: the lane's 16-byte plane chunks (row c, group 4*set + d)
     // and the scales (and zero points) of its output row c for the set's 4
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         }
     };
 
-    // Activation operands of the current set: XB[gi][4j+e] is the bf16 pair of
-    // columns 128g + 32d + 8j + 2e (+1) of batch row b0 + c.
+    // Activation operands of the current set: XB[sl][gi][4j+e] is the bf16 pair
+    // of columns 128g + 32d + 8j + 2e (+1) of batch row b0 + 16 sl + c.
     //
     // The lane needs 64 contiguous bytes of its row per group, but loading
     // them directly puts a wave's 16-byte pieces 64 bytes apart: each
@@ -185,134 +194,143 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     // are never stored; groups past k repeat the last group and have scale 0.
     // A load under a lane condition made the compiler wait for the
     // activations before issuing the plane loads.)
-    uint32_t XB[4][16];
+    uint32_t XB[NB][4][16];
     auto load_x = [&](int set) {
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-            const int gc = min(4 * set + gi, G - 1);
-            const uint16_t *xg = x + b0 * ldx + 128 * gc;
+        for (int sl = 0; sl < NB; ++sl)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t row = min((int64_t)(4 * j + d), batch - 1 - b0);
-                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xg + row * ldx + 8 * c);
-                XB[gi][4 * j] = v.x;
-                XB[gi][4 * j + 1] = v.y;
-                XB[gi][4 * j + 2] = v.z;
-                XB[gi][4 * j + 3] = v.w;
+            for (int gi = 0; gi < 4; ++gi) {
+                const int gc = min(4 * set + gi, G - 1);
+                const uint16_t *xg = x + b0 * ldx + 128 * gc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t row = min((int64_t)(16 * sl + 4 * j + d), batch - 1 - b0);
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xg + row * ldx + 8 * c);
+                    XB[sl][gi][4 * j] = v.x;
+                    XB[sl][gi][4 * j + 1] = v.y;
+                    XB[sl][gi][4 * j + 2] = v.z;
+                    XB[sl][gi][4 * j + 3] = v.w;
+                }
             }
-        }
     };
     // XB[gi][4j..4j+3] holds piece c of row 4j + d; afterwards piece 4d + j of
     // row c.  (In-order LDS access within a wave: no barrier.)
-    auto xstage = [&]() {
+    auto xstage = [&](uint32_t (&xs)[4][16]) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 *reinterpret_cast<u32x4_t *>(xbuf + (4 * j + d) * SMALLB_XROW + 16 * c) =
-                    u32x4_t{XB[gi][4 * j], XB[gi][4 * j + 1], XB[gi][4 * j + 2], XB[gi][4 * j + 3]};
+                    u32x4_t{xs[gi][4 * j], xs[gi][4 * j + 1], xs[gi][4 * j + 2], xs[gi][4 * j + 3]};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xbuf + c * SMALLB_XROW + 16 * (4 * d + j));
-                XB[gi][4 * j] = v.x;
-                XB[gi][4 * j + 1] = v.y;
-                XB[gi][4 * j + 2] = v.z;
-                XB[gi][4 * j + 3] = v.w;
+                xs[gi][4 * j] = v.x;
+                xs[gi][4 * j + 1] = v.y;
+                xs[gi][4 * j + 2] = v.z;
+                xs[gi][4 * j + 3] = v.w;
             }
         }
     };
-    // The chains' starting values: the correction of batch row 4d + v for
-    // group gi (init4[gi][v]), and for zero points the group sums of X
-    // (xsum4[gi][v]).  Each is formed in the lanes of its own batch row (row
-    // c), then moved to the lanes that hold that batch row's outputs through
-    // the LDS buffer.
-    f32x4_t init4[4], xsum4[ASYM ? 4 : 1];
+    // Corrections per batch row and group, formed in the lanes of their own
+    // batch row (row c of the slice): cr_d[sl] is the one of group 4*set + d,
+    // and for zero points xs_d[sl] the group sum of X.  Each step adds
+    // sum_g corr[b][g] * s[row][g] (and the zero-point term) to its outputs
+    // with one fp32 MFMA per slice (16x16x4: A = corrections, rows batch, k
+    // the set's four groups; B = scales, columns weight rows), so the chains
+    // start from zero.
+    float cr_d[NB], xs_d[NB];
     auto make_init = [&]() {
-        xstage();
-        float cr[4], sx[4];
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-            cr[gi] = sb_cross_row_sum(correction<R, 16>(XB[gi]));
-            if constexpr (ASYM) {
-                const uint32_t one = 0x3F803F80u;
-                float a = 0.f;
+        for (int sl = 0; sl < NB; ++sl) {
+            xstage(XB[sl]);
+            float cr[4], sx[4];
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
-                                                        __builtin_bit_cast(bf16x2_t, XB[gi][m]), a, false);
-                sx[gi] = sb_cross_row_sum(a);
+            for (int gi = 0; gi < 4; ++gi) {
+                cr[gi] = sb_cross_row_sum(correction<R, 16>(XB[sl][gi]));
+                if constexpr (ASYM) {
+                    const uint32_t one = 0x3F803F80u;
+                    float a = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m)
+                        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, one),
+                                                            __builtin_bit_cast(bf16x2_t, XB[sl][gi][m]), a, false);
+                    sx[gi] = sb_cross_row_sum(a);
+                }
             }
-        }
-        // (every quarter lane of row c writes the same values)
-        *reinterpret_cast<f32x4_t *>(xbuf + 16 * c) = f32x4_t{cr[0], cr[1], cr[2], cr[3]};
-        if constexpr (ASYM) *reinterpret_cast<f32x4_t *>(xbuf + 256 + 16 * c) = f32x4_t{sx[0], sx[1], sx[2], sx[3]};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const f32x4_t q = *reinterpret_cast<const f32x4_t *>(xbuf + 16 * (4 * d + v));
-#pragma unroll
-            for (int gi = 0; gi < 4; ++gi) init4[gi][v] = q[gi];
-            if constexpr (ASYM) {
-                const f32x4_t u = *reinterpret_cast<const f32x4_t *>(xbuf + 256 + 16 * (4 * d + v));
-#pragma unroll
-                for (int gi = 0; gi < 4; ++gi) xsum4[gi][v] = u[gi];
-            }
+            cr_d[sl] = d == 0 ? cr[0] : d == 1 ? cr[1] : d == 2 ? cr[2] : cr[3];
+            if constexpr (ASYM) xs_d[sl] = d == 0 ? sx[0] : d == 1 ? sx[1] : d == 2 ? sx[2] : sx[3];
         }
     };
 
-    auto compute = [&](int j) {
+    auto compute = [&](int j, f32x4_t (&out)[NB]) {
         // now pl[j][gi][p] = word d of row c's chunk of group 4*set + gi
 #pragma unroll
         for (int p = 0; p < R; ++p) sb_quad_transpose(pl[j][0][p], pl[j][1][p], pl[j][2][p], pl[j][3][p]);
-        f32x4_t out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sl = 0; sl < NB; ++sl) out[sl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             uint32_t D0[16], D1[16];
             decode_word<R>(pl[j][gi], D0, D1);
-            // activations are the A operand (rows: batch), weights the B
-            // operand (columns: weight rows): lane (c, d) ends with batch rows
-            // 4d..4d+3 of weight row c
-            f32x4_t P = init4[gi];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const u32x4_t xb = {XB[gi][4 * jj], XB[gi][4 * jj + 1], XB[gi][4 * jj + 2], XB[gi][4 * jj + 3]};
-                const u32x4_t a0 = {D0[4 * jj], D0[4 * jj + 1], D0[4 * jj + 2], D0[4 * jj + 3]};
-                P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb),
-                                                            __builtin_bit_cast(bf16x8_t, a0), P, 0, 0, 0);
-                if constexpr (NPH == 2) {
-                    const u32x4_t a1 = {D1[4 * jj], D1[4 * jj + 1], D1[4 * jj + 2], D1[4 * jj + 3]};
-                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb),
-                                                                __builtin_bit_cast(bf16x8_t, a1), P, 0, 0, 0);
-                }
-            }
             // (A group past k has scale 0; rows past n are never stored.)
             const uint32_t word = sw[j][gi >> 1];
-            const float s = sb_bf16_to_f32((gi & 1) ? (word >> 16) : (word & 0xFFFFu));
-            if constexpr (ASYM) {  // + (127.5 - z) * 2^(R-8) * sum of the group's X
-                const uint32_t zword = zw[j][gi >> 1];
-                const float z = sb_bf16_to_f32((gi & 1) ? (zword >> 16) : (zword & 0xFFFFu));
-                const float zc = (127.5f - z) * (1.0f / (float)(1 << (8 - R)));
+            const float sc = sb_bf16_to_f32((gi & 1) ? (word >> 16) : (word & 0xFFFFu));
 #pragma unroll
-                for (int v = 0; v < 4; ++v) P[v] = fmaf(zc, xsum4[gi][v], P[v]);
+            for (int sl = 0; sl < NB; ++sl) {
+                // activations are the A operand (rows: batch), weights the B
+                // operand (columns: weight rows): lane (c, d) ends with batch
+                // rows 4d..4d+3 of the slice for weight row c
+                f32x4_t P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const u32x4_t xb = {XB[sl][gi][4 * jj], XB[sl][gi][4 * jj + 1], XB[sl][gi][4 * jj + 2],
+                                        XB[sl][gi][4 * jj + 3]};
+                    const u32x4_t a0 = {D0[4 * jj], D0[4 * jj + 1], D0[4 * jj + 2], D0[4 * jj + 3]};
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb),
+                                                                __builtin_bit_cast(bf16x8_t, a0), P, 0, 0, 0);
+                    if constexpr (NPH == 2) {
+                        const u32x4_t a1 = {D1[4 * jj], D1[4 * jj + 1], D1[4 * jj + 2], D1[4 * jj + 3]};
+                        P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xb),
+                                                                    __builtin_bit_cast(bf16x8_t, a1), P, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) out[sl][v] = fmaf(sc, P[v], out[sl][v]);
             }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) out[v] = fmaf(s, P[v], out[v]);
         }
-        return out;
+        // The set's corrections (and zero-point terms): B = this lane's weight
+        // row c, group 4*set + d.
+        const uint32_t wd = (d >> 1) ? sw[j][1] : sw[j][0];
+        const float s_d = sb_bf16_to_f32((d & 1) ? (wd >> 16) : (wd & 0xFFFFu));
+#pragma unroll
+        for (int sl = 0; sl < NB; ++sl)
+            out[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(cr_d[sl], s_d, out[sl], 0, 0, 0);
+        if constexpr (ASYM) {  // + (127.5 - z) * 2^(R-8) * s * sum of the group's X
+            const uint32_t zd = (d >> 1) ? zw[j][1] : zw[j][0];
+            const float z = sb_bf16_to_f32((d & 1) ? (zd >> 16) : (zd & 0xFFFFu));
+            const float sz = s_d * ((127.5f - z) * (1.0f / (float)(1 << (8 - R))));
+#pragma unroll
+            for (int sl = 0; sl < NB; ++sl)
+                out[sl] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs_d[sl], sz, out[sl], 0, 0, 0);
+        }
     };
-    // Add a step's four outputs to this lane's slot for the tile.  One writer
-    // per slot (this lane), so no atomic is needed and the order of the
-    // additions is fixed: the wave's first set stores, later sets read, add
-    // and store.  (LDS float atomics serialize across the CU: four wave-wide
-    // ds_add_f32 per step doubled the kernel's time.)
-    auto commit = [&](int si, int t, const f32x4_t &v4) {
+    // Add a step's outputs (four per slice) to this lane's slots for the
+    // tile.  One writer per slot (this lane), so no atomic is needed and the
+    // order of the additions is fixed: the wave's first set stores, later sets
+    // read, add and store.  (LDS float atomics serialize across the CU: four
+    // wave-wide ds_add_f32 per step doubled the kernel's time.)
+    auto commit = [&](int si, int t, const f32x4_t (&o)[NB]) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float *p = &slot[(t * 4 + v) * 64 + lane];
-            if (si == 0)
-                *p = v4[v];
-            else
-                *p += v4[v];
-        }
+        for (int sl = 0; sl < NB; ++sl)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float *p = &slot[((t * NB + sl) * 4 + v) * 64 + lane];
+                if (si == 0)
+                    *p = o[sl][v];
+                else
+                    *p += o[sl][v];
+            }
     };
 
     // The wave's steps are (set ordinal si, tile t), set-major.  Loads run PD
@@ -350,9 +368,10 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
                 load_x(w + csi * W);
                 make_init();
             }
-            const f32x4_t v4 = compute(j);
+            f32x4_t o[NB];
+            compute(j, o);
             load_next(j);  // refill as soon as the buffer is free
-            commit(csi, ct, v4);
+            commit(csi, ct, o);
             if (++ct == T) {
                 ct = 0;
                 ++csi;
@@ -367,7 +386,9 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
                 load_x(w + csi * W);
                 make_init();
             }
-            commit(csi, ct, compute(j));
+            f32x4_t o[NB];
+            compute(j, o);
+            commit(csi, ct, o);
             if (++ct == T) {
                 ct = 0;
                 ++csi;
@@ -377,12 +398,12 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     // Outputs: add the waves' slots in a fixed order.
     __syncthreads();
     const float post = (float)(1 << (8 - R));
-    for (int e = threadIdx.x; e < T * 256; e += blockDim.x) {
-        const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
+    for (int e = threadIdx.x; e < T * NB * 256; e += blockDim.x) {
+        const int ts = e >> 8, v = (e >> 6) & 3, l = e & 63;  // ts = t * NB + slice
         float sum = 0.f;
-        for (int ww = 0; ww < W; ++ww) sum += red[((size_t)ww * tiles_per_wg + t) * 256 + v * 64 + l];
-        const int row = 16 * (t_begin + t) + (l & 15);
-        const int64_t b = b0 + 4 * (l >> 4) + v;
+        for (int ww = 0; ww < W; ++ww) sum += red[((size_t)ww * tiles_per_wg * NB + ts) * 256 + v * 64 + l];
+        const int row = 16 * (t_begin + ts / NB) + (l & 15);
+        const int64_t b = b0 + 16 * (ts % NB) + 4 * (l >> 4) + v;
         if (row < n && b < batch) store_y(y, ybf16, b * ldy + row, sum * post);
     }
 }
@@ -396,32 +417,56 @@ static int smallb_tpw(const QgemmArgs &a, int cu_count) {
     return tpw;
 }
 
-template <int R, bool ASYM, bool S4>
+// Batch rows per pass over the planes: 32 (two slices per workgroup) where
+// the second slice's activations fit in registers (r <= 4) and its partial
+// sums in LDS, else 16.
+int smallb_pass_rows(int r, int n, int cu_count) {
+    QgemmArgs a = {};
+    a.n = n;
+    return r <= 4 && smallb_tpw(a, cu_count) <= SMALLB_NB2_MAX_TILES ? 32 : 16;
+}
+
+static int smallb_nb(int r, const QgemmArgs &a, int cu_count) {
+    return a.batch > 16 && smallb_pass_rows(r, a.n, cu_count) == 32 ? 2 : 1;
+}
+
+template <int R, bool ASYM, bool S4, int NB>
 static void launch_v(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int tiles = (a.n + 15) / 16;
     const int tpw = smallb_tpw(a, cu_count);
-    dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)((a.batch + 15) / 16));
-    hipLaunchKernelGGL((smallb_kernel<R, SMALLB_DEPTH, ASYM, S4>), grid, dim3(64 * SMALLB_WAVES),
-                       smallb_lds_bytes(SMALLB_WAVES, tpw), stream, a.x, a.batch, a.ldx, a.planes,
+    dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)((a.batch + 16 * NB - 1) / (16 * NB)));
+    hipLaunchKernelGGL((smallb_kernel<R, SMALLB_DEPTH, ASYM, S4, NB>), grid, dim3(64 * SMALLB_WAVES),
+                       smallb_lds_bytes(SMALLB_WAVES, tpw, NB), stream, a.x, a.batch, a.ldx, a.planes,
                        a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, tpw, a.y, a.ldy, a.ybf16);
 }
 
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const bool s4 = ((a.k / 128) & 3) == 0;
+    if constexpr (R <= 4) {
+        if (smallb_nb(R, a, cu_count) == 2) {
+            if (a.zeros) {
+                if (s4) launch_v<R, true, true, 2>(a, cu_count, stream);
+                else launch_v<R, true, false, 2>(a, cu_count, stream);
+            } else {
+                if (s4) launch_v<R, false, true, 2>(a, cu_count, stream);
+                else launch_v<R, false, false, 2>(a, cu_count, stream);
+            }
+            return;
+        }
+    }
     if (a.zeros) {
-        if (s4) launch_v<R, true, true>(a, cu_count, stream);
-        else launch_v<R, true, false>(a, cu_count, stream);
+        if (s4) launch_v<R, true, true, 1>(a, cu_count, stream);
+        else launch_v<R, true, false, 1>(a, cu_count, stream);
     } else {
-        if (s4) launch_v<R, false, true>(a, cu_count, stream);
-        else launch_v<R, false, false>(a, cu_count, stream);
+        if (s4) launch_v<R, false, true, 1>(a, cu_count, stream);
+        else launch_v<R, false, false, 1>(a, cu_count, stream);
     }
 }
 
 void smallb_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
-    (void)cu_count;
-    snprintf(out, len, "nbw::smallb_kernel<%d, %d, %s, %s>", r, SMALLB_DEPTH, a.zeros ? "true" : "false",
-             ((a.k / 128) & 3) == 0 ? "true" : "false");
+    snprintf(out, len, "nbw::smallb_kernel<%d, %d, %s, %s, %d>", r, SMALLB_DEPTH, a.zeros ? "true" : "false",
+             ((a.k / 128) & 3) == 0 ? "true" : "false", smallb_nb(r, a, cu_count));
 }
 
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {

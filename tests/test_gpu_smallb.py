@@ -1,4 +1,5 @@
-"""GPU parity of the small-batch kernel where its step order crosses set boundaries.
+"""GPU parity of the small-batch kernel where its step order crosses set boundaries,
+and of the automatic choice between it and the large-batch GEMM.
 
 The kernel walks (set, tile) steps set-major and prefetches planes and scales
 across set boundaries; a workgroup holds a run of tiles and each wave several
@@ -75,5 +76,27 @@ def test_smallb_set_boundaries_asym(nbw, case):
     y = nbw.qgemm(x, w.slice_view(r), s, r, zeros=zd).cpu().numpy()
     ref = oracle.qgemm_asym(xb, oracle.pack(case["codes"]), case["scales"], z, N, K, r)
     e = rel_err(y, ref)
+    print(f"  err={e:.3e}", flush=True)
+    assert e <= CONTRACT and e <= DESIGN_BOUND
+
+
+# The automatic choice: the small-batch kernel while it needs one pass over the
+# planes (32 batch rows a pass for r <= 4 on short tile runs, 16 otherwise), or
+# two passes with k <= 8192; the large-batch GEMM beyond.
+@pytest.mark.parametrize("batch,k,r,family", [
+    (17, 1024, 3, "smallb"), (32, 1024, 3, "smallb"), (33, 1024, 3, "smallb"), (64, 1024, 3, "smallb"),
+    (65, 1024, 3, "gemm"), (32, 8320, 3, "smallb"), (33, 8320, 3, "gemm"),
+    (17, 1024, 6, "smallb"), (32, 1024, 6, "smallb"), (33, 1024, 6, "gemm"), (17, 8320, 6, "gemm")])
+def test_auto_dispatch_boundaries(nbw, batch, k, r, family):
+    n = 300
+    name = nbw.kernel_name(batch, n, k, r)
+    print(f"auto n={n} k={k} batch={batch} r={r}: {name}", flush=True)
+    assert name.startswith(f"nbw::{family}_kernel")
+    c = synth.random_case(n, k, batch, seed=80 + batch, recipe="gptq_like", outliers=True)
+    w = nbw.pack_bitplanes(torch.from_numpy(c["codes"]).cuda())
+    x = torch.from_numpy(c["x"]).view(torch.bfloat16).cuda()
+    s = torch.from_numpy(c["scales"]).view(torch.bfloat16).cuda()
+    y = nbw.qgemm(x, w.slice_view(r), s, r).cpu().numpy()
+    e = rel_err(y, oracle.qgemm(c["x"], oracle.pack(c["codes"]), c["scales"], n, k, r))
     print(f"  err={e:.3e}", flush=True)
     assert e <= CONTRACT and e <= DESIGN_BOUND
