@@ -24,7 +24,8 @@ read of the same plane bytes takes in one launch (nbw_stream_read, same rotation
 and timing: the floor a launch of that size cannot beat, well under the 8 TB/s
 peak for tens of MB); the 12 products as 3 grouped dispatches; batch 4
 and 16 on the same linears; batch 256 (TFLOP/s, r in 8, 4, 3, 2, activations
-with 1% outlier channels x10); batch 1 on the largest single linears (70B-shaped
+with 1% outlier channels x10) and the rest of that sweep, batch 32, 64 and 128
+through the automatic kernel choice (``batch_sweep``); batch 1 on the largest single linears (70B-shaped
 gate_up and down, Qwen3-8B-shaped gate_up: plane bytes worth >= 5 us at the HBM
 peak) with their read floors (``large_b1``); dense bf16 torch.matmul (hipBLASLt) on
 the Llama linears at batch 1 and 256 with the sliced products' speedup over it
@@ -548,6 +549,30 @@ def main():
                                                              / 1e12, 1)}
                                             for (nm, r), d in sorted(d256.items())]}
         log(f"batch 256: {tflops:.1f} TFLOP/s; {n256} {ach256:.1f} TFLOP/s")
+
+        # ---- the rest of the large-batch sweep (batch 32, 64, 128; r = 8, 4, 3, 2; activations
+        # with outlier channels), through the automatic kernel choice: time per step of the 16
+        # products, TFLOP/s, plane bytes per second, and the kernel family each product used
+        sweep = {}
+        for b in (32, 64, 128):
+            for sid, L in enumerate(layer.lin):
+                d = synth.activations(b, L["k"], synth.rng_for(0, wid, sid, synth.T_X), outliers=True,
+                                      outlier_rng=synth.rng_for(0, wid, sid, synth.T_OUTLIERS))
+                L[f"x{b}"] = torch.from_numpy(d).view(torch.bfloat16).cuda()
+                L[f"y{b}"] = torch.empty((b, L["n"]), dtype=torch.float32, device="cuda")
+            stb = Stepper(torch, nbw, layer, RS_B256, f"x{b}", f"y{b}")
+            msb = stb.time(max(4, args.steps // 20), 2, graph=True)
+            del stb
+            fl = sum(2 * b * L["n"] * L["k"] for _ in RS_B256 for L in layer.lin)
+            pb = sum(r * L["n"] * L["k"] // 8 for r in RS_B256 for L in layer.lin)
+            fams = sorted({nbw.kernel_name(b, L["n"], L["k"], r).split("<")[0].replace("nbw::", "")
+                           for r in RS_B256 for L in layer.lin})
+            sweep[f"batch{b}"] = {"ms_per_step": round(msb, 5), "TFLOPs": round(fl / (msb * 1e-3) / 1e12, 1),
+                                  "plane_GBps": round(pb / (msb * 1e-3) / 1e9, 1), "kernels": fams}
+            for L in layer.lin:
+                del L[f"x{b}"], L[f"y{b}"]
+            log(f"batch {b}: {sweep[f'batch{b}']}")
+        result["batch_sweep"] = sweep
 
         # ---- batch 1 on the largest single linears (70B-shaped gate_up and down at r = 3, 2;
         # Qwen3-8B-shaped gate_up at r = 6, 4): the shapes whose plane bytes take >= 5 us at the
