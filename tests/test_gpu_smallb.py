@@ -10,7 +10,10 @@ sets.  These shapes make every boundary case meet in one launch:
   one group (the three groups past k carry scale 0 and repeated activations);
   9 sets over 8 waves, so wave 0 runs two sets;
 * batch 7 (rows past the batch in the MFMA tile) and 16, r = 3 and 5 (one and
-  two decode phases), plus zero points.
+  two decode phases), plus zero points;
+* batch 25 and 32 at r = 3: two 16-row slices per workgroup (32 batch rows per
+  pass over the planes), the second one partly past the batch at 25; and with
+  zero points at batch 29.
 
 Every output is compared with the fp64 oracle.  Bars as in test_gpu_parity.
 """
@@ -38,7 +41,7 @@ def nbw():
 
 @pytest.fixture(scope="module")
 def case():
-    return synth.random_case(N, K, 16, seed=77, recipe="gptq_like", outliers=True)
+    return synth.random_case(N, K, 32, seed=77, recipe="gptq_like", outliers=True)
 
 
 def rel_err(y, ref):
@@ -47,11 +50,12 @@ def rel_err(y, ref):
     return float((np.abs(y - ref).max(axis=1) / den).max())
 
 
-@pytest.mark.parametrize("batch", [7, 16])
-@pytest.mark.parametrize("r", [3, 5])
+@pytest.mark.parametrize("batch,r", [(7, 3), (16, 3), (7, 5), (16, 5), (25, 3), (32, 3)])
 def test_smallb_set_boundaries_every_output(nbw, case, batch, r):
     print(f"smallb n={N} k={K} batch={batch} r={r}", flush=True)
-    assert nbw.kernel_name(batch, N, K, r).startswith("nbw::smallb_kernel")
+    name = nbw.kernel_name(batch, N, K, r)
+    print(f"  {name}", flush=True)
+    assert name.startswith("nbw::smallb_kernel") and name.endswith(", 2>" if batch > 16 else ", 1>")
     w = nbw.pack_bitplanes(torch.from_numpy(case["codes"]).cuda())
     xb = np.ascontiguousarray(case["x"][:batch])
     x = torch.from_numpy(xb).view(torch.bfloat16).cuda()
@@ -63,8 +67,9 @@ def test_smallb_set_boundaries_every_output(nbw, case, batch, r):
     assert e <= CONTRACT and e <= DESIGN_BOUND
 
 
-def test_smallb_set_boundaries_asym(nbw, case):
-    batch, r = 9, 4
+@pytest.mark.parametrize("batch", [9, 29])
+def test_smallb_set_boundaries_asym(nbw, case, batch):
+    r = 4
     print(f"smallb asym n={N} k={K} batch={batch} r={r}", flush=True)
     rng = np.random.default_rng(78)
     z = synth.f32_to_bf16_bits(rng.integers(96, 160, size=(N, K // 128)).astype(np.float32))
