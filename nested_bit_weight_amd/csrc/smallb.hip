@@ -2,7 +2,8 @@
 //
 // Same product as gemv.hip (MatGPTQ: Efficient and Accurate Inference over
 // Nested Quantized Models, Abstract: kernels supporting batch sizes beyond
-// one; Figure 1: batch sweep), for 2..16 batch rows per launch slice.  Beyond
+// one; Figure 1: batch sweep), for small batches: 16 batch rows per pass over
+// the planes, or 32 (two slices) for r <= 4.  Beyond
 // one batch row the bf16 dot products would take more VALU issue slots than
 // the plane decode itself, so the contraction moves to the matrix cores; the
 // product is still bound by HBM, so the kernel streams like the batch-1 one:
@@ -26,17 +27,19 @@
 //    workgroup per CU); its waves split k into 4-group sets (wave w: sets w,
 //    w+W, ...).  A wave's steps are (set, tile) pairs, set-major: when a set
 //    starts, the wave loads its activation operands (16 batch rows x 512
-//    columns, 64 registers per lane), and the planes and scales run PD steps
-//    ahead across set boundaries.  Loads are unconditional (clamped at the
-//    end), so the loads in flight between a load and its use are a static
-//    count.
+//    columns per slice, 64 registers per lane), and the planes and scales
+//    run PD steps ahead across set boundaries.  Loads are unconditional
+//    (clamped at the end), so the loads in flight between a load and its use
+//    are a static count.
+//  - with two slices (NB = 2), every decoded weight fragment feeds the MFMAs
+//    of both, so the plane decode is paid once per 32 batch rows.
 //  - every MFMA chain covers one 128-wide group and starts from zero; the
 //    group scale is folded in fp32 right after it (one FMA per output), and
 //    the corrections that remove the decoded operands' constant offsets
 //    enter through one fp32 MFMA per step (corrections x scales over the
 //    set's four groups).
-//  - each lane adds its four outputs of a step to its own LDS slot for the
-//    tile; the waves meet there at the end.
+//  - each lane adds its four outputs per slice of a step to its own LDS
+//    slots for the tile; the waves meet there at the end.
 #include <cstdio>
 
 #include "decode.h"
