@@ -73,6 +73,12 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="derive per-launch HBM traffic from two rocprofv3 --pmc output folders "
                          "of --pmc-probe and write it under profiles/")
+    ap.add_argument("--pmc-rbits", action="store_true",
+                    help="run only a plain device copy and the batch-1 gate_up product at r = 1..8 "
+                         "(for a rocprofv3 --pmc FETCH_SIZE pass)")
+    ap.add_argument("--rbits-from", metavar="FETCH_DIR",
+                    help="bytes fetched per child width from a FETCH_SIZE pass of --pmc-rbits, "
+                         "written under profiles/")
     return ap.parse_args()
 
 
@@ -270,6 +276,66 @@ def pmc_probe(torch, nbw, synth):
         f"x {PROBE_LAUNCHES} on {PROBE_SHAPES}")
 
 
+RBITS_FILE = os.path.join(ROOT, "profiles", "fetch_by_r_gemv_gate_up_b1.txt")
+RBITS_RS = (1, 2, 3, 4, 5, 6, 7, 8)
+
+
+def pmc_rbits_probe(torch, nbw, synth):
+    """The reference copy, then the batch-1 product on the Llama-3.1-8B gate_up
+    linear at every child width, one launch per parent copy (for a FETCH_SIZE
+    pass: bytes fetched from memory against r/8 bytes per weight)."""
+    src = torch.empty(PROBE_COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    layer = Layer(torch, nbw, synth, "llama3.1-8b", PROBE_LAUNCHES)
+    L = next(L for L in layer.lin if L["name"] == "gate_up")
+    y = torch.empty((1, L["n"]), dtype=torch.float32, device="cuda")
+    for r in RBITS_RS:
+        for c in range(layer.copies):
+            nbw.qgemm(L["x1"], L["w"][c].slice_view(r), L["s"][c], r, out=y)
+            torch.cuda.synchronize()
+    log(f"pmc r-bits probe: copy {PROBE_COPY_BYTES} B; gate_up batch 1, r = {RBITS_RS}, "
+        f"{layer.copies} launches each")
+
+
+def rbits_from(fetch_dir):
+    import synth
+    rows = _pmc_rows(fetch_dir, "FETCH_SIZE")
+    copy = [v for _, name, v in rows if "copybuffer" in name.lower()]
+    if not copy:
+        raise SystemExit(f"the reference copy is not in {fetch_dir}")
+    factor = PROBE_COPY_BYTES / (max(copy) * 1024.0)
+    n, k = next((n, k) for nm, n, k in synth.WORKLOADS["llama3.1-8b"] if nm == "gate_up")
+    lines = [
+        f"# Bytes fetched from memory by the batch-1 product on the Llama-3.1-8B gate_up linear ({n} x {k}) at each child width",
+        "",
+        "Commands (repository root, one MI355X):",
+        "  rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_rbits -- python3 bench.py --pmc-rbits",
+        "  python3 bench.py --rbits-from gpurun_out/pmc_rbits",
+        "",
+        f"FETCH_SIZE scaled by what it reads for a plain copy of {PROBE_COPY_BYTES} bytes: factor {factor:.4f}",
+        "planes = r n k / 8 bytes; scales = n k / 64 bytes (bf16, one per 128 weights); X = 2 k bytes",
+        "",
+        "| r | kernel | launches | fetched bytes | planes + scales + X | fetched / (planes + scales + X) | fetched / planes |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for r in RBITS_RS:
+        kern = [(name, v) for _, name, v in rows if f"gemv_kernel<{r}," in name]
+        if not kern:
+            raise SystemExit(f"r={r}: no gemv_kernel<{r}, *> dispatches in {fetch_dir}")
+        avg = sum(v for _, v in kern) / len(kern) * 1024.0 * factor
+        planes = r * n * k // 8
+        expect = planes + n * k // 64 + 2 * k
+        kname = kern[0][0].split("(")[0].replace("void ", "")
+        lines.append(f"| {r} | `{kname}` | {len(kern)} | {avg:.0f} | {expect} | {avg / expect:.4f} | {avg / planes:.4f} |")
+    with open(RBITS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _pmc_rows(folder, counter):
     import csv
     import glob
@@ -343,6 +409,9 @@ def main():
     if args.traffic_from:
         traffic_from(*args.traffic_from)
         return
+    if args.rbits_from:
+        rbits_from(args.rbits_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -363,6 +432,9 @@ def main():
 
     if args.pmc_probe:
         pmc_probe(torch, nbw, synth)
+        return
+    if args.pmc_rbits:
+        pmc_rbits_probe(torch, nbw, synth)
         return
 
     t = time.time()
