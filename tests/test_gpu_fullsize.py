@@ -3,7 +3,7 @@
 * the single 1024 x 1024 linear (uniform parent codes, scales U(0.001, 0.01),
   X ~ N(0, 1), batch 1, r = 8, 4, 2): every output against the fp64 oracle,
   on every kernel;
-* the Qwen3-8B-shaped linears (batch 1, 4, 32, 256; r = 6, 4, 3, 2) and the
+* the Qwen3-8B-shaped linears (batch 1, 4, 32, 64, 256; r = 6, 4, 3, 2) and the
   70B-shaped layer (batch 1, 16, 128; r = 3, 2) at full size, through the
   automatic kernel choice (the launch configuration the bench times): the
   output rows of the first and last tiles plus 59 seeded rows against the
@@ -90,7 +90,7 @@ def _sampled(nbw, workload, shape_id, batches, rs):
 
 @pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
 def test_qwen3_8b_full_size_sampled(nbw, shape_id):
-    _sampled(nbw, "qwen3-8b", shape_id, (1, 4, 32, 256), (6, 4, 3, 2))
+    _sampled(nbw, "qwen3-8b", shape_id, (1, 4, 32, 64, 256), (6, 4, 3, 2))
 
 
 @pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
