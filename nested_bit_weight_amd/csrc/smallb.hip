@@ -243,7 +243,9 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     // the set's four groups; B = scales, columns weight rows), so the chains
     // start from zero.
     float cr_d[NB], xs_d[NB];
-    auto make_init = [&]() {
+    // A set's start: its activations into the operand layout, then its
+    // corrections (waits for the activations only).
+    auto start_set = [&]() {
 #pragma unroll
         for (int sl = 0; sl < NB; ++sl) {
             xstage(XB[sl]);
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
             load_next(j);
         }
         __builtin_amdgcn_sched_barrier(0);
-        make_init();  // (waits for the activations only: they were issued first)
+        start_set();  // (waits for the activations only: they were issued first)
         __builtin_amdgcn_sched_barrier(0);
     }
     int csi = 0, ct = 0;  // the step being computed
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         for (int j = 0; j < PD; ++j) {
             if (ct == 0 && csi > 0) {
                 load_x(w + csi * W);
-                make_init();
+                start_set();
             }
             f32x4_t o[NB];
             compute(j, o);
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
         if (nfull + j < nsteps) {
             if (ct == 0 && csi > 0) {
                 load_x(w + csi * W);
-                make_init();
+                start_set();
             }
             f32x4_t o[NB];
             compute(j, o);
