@@ -33,6 +33,12 @@ MUTANTS = {
     "wrong_sign": ("acc += nbwo_bf16_to_double", "acc -= nbwo_bf16_to_double"),
     "lsb_first_unpack": ("v = 2 * v + read_bit(planes, n, k, p, i, j);",
                          "v = v + (read_bit(planes, n, k, p, i, j) << p);"),
+    "padding_rows_ones": ("for (int64_t i = 0; i < n; ++i)\n            for (int64_t j = 0; j < k; ++j) {\n"
+                          "                int b = (codes[i * k + j] >> (7 - p)) & 1;",
+                          "for (int64_t i = 0; i < padded_rows(n); ++i)\n            for (int64_t j = 0; j < k; ++j) {\n"
+                          "                int b = i < n ? ((codes[i * k + j] >> (7 - p)) & 1) : 1;"),
+    "sampled_row_shifted": ("qgemm_row(x, batch, planes, scales, n, k, r, rows[t], wrow, y + t, nrows);",
+                            "qgemm_row(x, batch, planes, scales, n, k, r, (rows[t] + 1) % n, wrow, y + t, nrows);"),
     # asymmetric children
     "asym_dropped_half": ("((double)q + 0.5) - 0.5 - z)", "((double)q + 0.5) - z)"),
     "asym_zero_sign": ("((double)q + 0.5) - 0.5 - z)", "((double)q + 0.5) - 0.5 + z)"),
@@ -53,7 +59,9 @@ def _pin_calls():
              pins.test_dequant_r8_is_parent_grid,
              lambda: pins.test_qgemm_exact_rational_bruteforce(3),
              lambda: pins.test_qgemm_second_route_without_planes(4),
-             lambda: pins.test_qgemm_identity_activations_give_weights(4)]
+             lambda: pins.test_qgemm_identity_activations_give_weights(4),
+             pins.test_padding_rows_are_zero_bits,
+             pins.test_qgemm_rows_equals_full]
     for row in pins._golden_layout():
         calls.append(lambda row=row: pins.test_layout_worked_examples(*row))
     calls += [lambda: pins_ext.test_asym_with_midpoint_zero_is_symmetric(3),
