@@ -9,9 +9,11 @@ parent (host-only view) and run qgemm on all four linears -- 12 launches that
 read r/8 bytes per weight of bit-planes.  ``value`` is plane bytes read per
 second over the timed steps (whole job, inputs resident in HBM).
 
-A decode step is a chain of short launches, so the step is captured once into a
-HIP graph per parent copy and replayed (``value``); the same step launched from
-Python one call at a time is reported as ``eager``.  Packing is once per
+A decode step is a chain of short launches, so the steps of one rotation over
+the parent copies are captured into one HIP graph (a chain of steps, as a
+captured multi-layer pass would be) and replayed, with a graph of the first m
+steps for the remainder so that exactly --steps steps run (``value``); the same
+step launched from Python one call at a time is reported as ``eager``.  Packing is once per
 checkpoint and is timed separately (``pack`` field).
 
 To measure HBM and not the 256 MB MALL, every (step, r) uses its own parent
@@ -22,7 +24,8 @@ graph over the copy rotation, HIP events around the replays) giving the
 dominant kernel's roofline, and beside each product the time a plain streaming
 read of the same plane bytes takes in one launch (nbw_stream_read, same rotation
 and timing: the floor a launch of that size cannot beat, well under the 8 TB/s
-peak for tens of MB); the 12 products as 3 grouped dispatches; batch 4
+peak for tens of MB); the 12 products as 3 grouped dispatches, and as one
+mixed-precision dispatch (``grouped_mixed``); batch 4
 and 16 on the same linears; batch 256 (TFLOP/s, r in 8, 4, 3, 2, activations
 with 1% outlier channels x10) and the rest of that sweep, batch 32, 64 and 128
 through the automatic kernel choice (``batch_sweep``); batch 1 on the largest single linears (70B-shaped
@@ -124,7 +127,13 @@ def step_calls(nbw, layer, rs, step, xkey, ykey, kernel):
 
 
 def capture(torch, fn):
-    """fn() captured into a HIP graph (fn launches on the current stream)."""
+    """fn() captured into a HIP graph (fn launches on the current stream) and
+    launched once.
+
+    Python's cycle collector is held off during the capture (after a collection
+    outside it): a graph freed by the collector mid-capture would be destroyed
+    while the stream captures, which HIP refuses."""
+    import gc
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -132,8 +141,15 @@ def capture(torch, fn):
         fn()  # once eagerly on a side stream before capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        fn()
+    gc.collect()
+    gc.disable()
+    try:
+        with torch.cuda.graph(g):
+            fn()
+    finally:
+        gc.enable()
+    torch.cuda.synchronize()
+    g.replay()  # the first launch uploads the graph: part of making it, never timed
     torch.cuda.synchronize()
     return g
 
@@ -151,49 +167,97 @@ def event_time(torch, body, steps):
     return t0.elapsed_time(t1) / steps
 
 
+# Rotations of the parent copies captured into one graph where a batch-1
+# product is timed back to back (per-product durations, read floors, the large
+# linears): the gap between graph launches is a visible share of launches of a
+# few us.  Batch-1, -4 and -16 steps likewise run as chains of steps
+# (PeriodGraph).  The large-batch timings keep one graph per step and one
+# rotation per product graph: measured on one box, longer chains of batch-256
+# products ran slower (step 564-570 against 600-607 TFLOP/s).
+GRAPH_ROTATIONS = 4
+
+
+class PeriodGraph:
+    """Steps 0..period-1 of a copy rotation captured as ONE graph (a chain of
+    steps, as a captured multi-layer pass would be), plus graphs of the first m
+    steps for the remainder, so that exactly N steps replay.  (A graph per step
+    left a gap of ~4-5 us between consecutive graph launches: 89 against 85 us
+    per batch-1 step.)"""
+
+    def __init__(self, torch, step_fn, period):
+        self.torch, self.step_fn, self.period = torch, step_fn, period
+        self.full = capture(torch, lambda: [step_fn(j) for j in range(period)])
+        self.part = {}
+
+    def _part(self, m):
+        if m not in self.part:
+            self.part[m] = capture(self.torch, lambda: [self.step_fn(j) for j in range(m)])
+        return self.part[m]
+
+    def run(self, steps):
+        full, rem = divmod(steps, self.period)
+        for _ in range(full):
+            self.full.replay()
+        if rem:
+            self._part(rem).replay()
+
+    def time(self, steps, warmup):
+        """ms per step over exactly `steps` steps, after `warmup` untimed ones."""
+        if warmup:
+            self.run(warmup)
+        if steps % self.period:
+            self._part(steps % self.period)  # captured before the timed region
+        return event_time(self.torch, lambda i: self.run(steps), 1) / steps
+
+
 class Stepper:
-    """One step (every r x every linear) as prepared calls and as HIP graphs.
+    """One step (every r x every linear) as prepared calls and as HIP graphs:
+    with ``chain`` the copy rotation's steps as one PeriodGraph (for short,
+    launch-bound steps), else one graph per step (step i and step i + copies
+    are the same launches, so one graph per residue covers every step)."""
 
-    Step i and step i + copies are the same launches, so one graph per residue
-    modulo the rotation covers every step."""
-
-    def __init__(self, torch, nbw, layer, rs, xkey, ykey, kernel="auto", graphs=True):
+    def __init__(self, torch, nbw, layer, rs, xkey, ykey, kernel="auto", chain=False):
         self.torch = torch
         self.period = layer.copies
         self.calls = [step_calls(nbw, layer, rs, j, xkey, ykey, kernel) for j in range(self.period)]
-        self.graphs = None
-        if graphs:
-            self.graphs = [capture(torch, lambda cl=cl: [c() for c in cl]) for cl in self.calls]
+        # (closures over the calls, not bound methods: no reference cycle
+        # through self, so the graphs go as soon as the stepper does)
+        calls, period = self.calls, self.period
+        self.pg = PeriodGraph(torch, lambda i: [c() for c in calls[i % period]], period) if chain else None
+        self.graphs = None if chain else [capture(torch, lambda cl=cl: [c() for c in cl]) for cl in calls]
 
     def eager(self, i):
         for c in self.calls[i % self.period]:
             c()
 
-    def replay(self, i):
-        self.graphs[i % self.period].replay()
-
     def time(self, steps, warmup, graph=True):
-        body = self.replay if graph else self.eager
+        if graph and self.pg is not None:
+            return self.pg.time(steps, warmup)
+        if graph:
+            g, P = self.graphs, self.period
+            body = lambda i: g[i % P].replay()  # noqa: E731
+        else:
+            body = self.eager
         for i in range(warmup):
             body(i)
         return event_time(self.torch, lambda i: body(warmup + i), steps)
 
 
-def kernel_durations(torch, nbw, layer, rs, xkey, ykey, batch, kernel, reps):
+def kernel_durations(torch, nbw, layer, rs, xkey, ykey, batch, kernel, reps, rotations=1):
     """Back-to-back duration of every product of the step.
 
     For each (linear, r) a graph holds that product once per parent copy (so no
-    launch re-reads what the previous one left in cache); the graph is replayed
-    ``reps`` times between two HIP events.  Returns {(linear, r): us per launch}."""
+    launch re-reads what the previous one left in cache), ``rotations`` times
+    over; the graph is replayed ``reps`` times between two HIP events.  Returns
+    {(linear, r): us per launch}."""
     out = {}
     for r in rs:
         for L in layer.lin:
             calls = [nbw.QgemmCall(L[xkey], L["w"][c].slice_view(r), L["s"][c], r, out=L[ykey],
                                    kernel=kernel) for c in range(layer.copies)]
-            g = capture(torch, lambda cl=calls: [c() for c in cl])
-            g.replay()
+            g = capture(torch, lambda cl=calls: [c() for _ in range(rotations) for c in cl])
             ms = event_time(torch, lambda i: g.replay(), reps)
-            out[(L["name"], r)] = {"us": ms * 1e3 / len(calls), "n": L["n"], "k": L["k"],
+            out[(L["name"], r)] = {"us": ms * 1e3 / (len(calls) * rotations), "n": L["n"], "k": L["k"],
                                    "kernel": nbw.kernel_name(batch, L["n"], L["k"], r, kernel)}
             del g
     return out
@@ -212,10 +276,11 @@ def stream_floor(torch, nbw, layer, rs, reps):
         for L in layer.lin:
             nbytes = r * L["w"][0].plane_bytes
             bufs = [L["w"][c].storage for c in range(layer.copies)]
-            g = capture(torch, lambda bl=bufs, nb=nbytes: [nbw.stream_read(b, nb, sink) for b in bl])
+            g = capture(torch, lambda bl=bufs, nb=nbytes: [nbw.stream_read(b, nb, sink)
+                                                           for _ in range(GRAPH_ROTATIONS) for b in bl])
             g.replay()
             ms = event_time(torch, lambda i: g.replay(), reps)
-            out[(L["name"], r)] = ms * 1e3 / len(bufs)
+            out[(L["name"], r)] = ms * 1e3 / (len(bufs) * GRAPH_ROTATIONS)
             del g
     return out
 
@@ -446,7 +511,7 @@ def main():
 
     # ---- headline: batch 1, r = 4, 3, 2, the step replayed as a HIP graph
     bytes_step = sum(r * L["n"] * L["k"] // 8 for r in RS_B1 for L in layer.lin)
-    st1 = Stepper(torch, nbw, layer, RS_B1, "x1", "y1", args.b1_kernel)
+    st1 = Stepper(torch, nbw, layer, RS_B1, "x1", "y1", args.b1_kernel, chain=True)
     ms = st1.time(args.steps, args.warmup, graph=True)
     value = bytes_step / (ms * 1e-3) / 1e9
     log(f"batch 1 (graph): {ms * 1e3:.1f} us/step, {value:.1f} GB/s")
@@ -454,7 +519,7 @@ def main():
     log(f"batch 1 (eager): {ms_eager * 1e3:.1f} us/step, {bytes_step / (ms_eager * 1e-3) / 1e9:.1f} GB/s")
     del st1
 
-    durs = kernel_durations(torch, nbw, layer, RS_B1, "x1", "y1", 1, args.b1_kernel,
+    durs = kernel_durations(torch, nbw, layer, RS_B1, "x1", "y1", 1, args.b1_kernel, rotations=GRAPH_ROTATIONS,
                             reps=max(10, args.steps // 4))
     dom_name, dom = dominant(durs, 1)
     dom_avg_us = dom["us"] / dom["launches"]
@@ -504,15 +569,35 @@ def main():
             c = copy_of(layer, RS_B1, step, ri)
             nbw.qgemm_grouped([(L["x1"], L["w"][c].slice_view(r), L["s"][c], r) for L in layer.lin],
                               outs=[L["y1"] for L in layer.lin])
-    ggraphs = [capture(torch, lambda j=j: grouped_step(j)) for j in range(layer.copies)]
-    for i in range(args.warmup):
-        ggraphs[i % layer.copies].replay()
-    gms = event_time(torch, lambda i: ggraphs[(args.warmup + i) % layer.copies].replay(), args.steps)
-    del ggraphs
+    gpg = PeriodGraph(torch, grouped_step, layer.copies)
+    gms = gpg.time(args.steps, args.warmup)
+    del gpg
     result["grouped"] = {"GBps": round(bytes_step / (gms * 1e-3) / 1e9, 1), "ms_per_step": round(gms, 5),
                          "dispatches_per_step": len(RS_B1),
                          "note": "4 linears per dispatch, one dispatch per r; independent products"}
     log(f"batch 1 grouped: {gms * 1e3:.1f} us/step, {result['grouped']['GBps']} GB/s")
+
+    # ---- all 12 products (every linear at every r) as ONE grouped dispatch, each product
+    # with its own output: mixed precision in a single launch
+    ymix = {(L["name"], r): torch.empty((1, L["n"]), dtype=torch.float32, device="cuda")
+            for L in layer.lin for r in RS_B1}
+
+    def mixed_step(step):
+        items, outs = [], []
+        for ri, r in enumerate(RS_B1):
+            c = copy_of(layer, RS_B1, step, ri)
+            for L in layer.lin:
+                items.append((L["x1"], L["w"][c].slice_view(r), L["s"][c], r))
+                outs.append(ymix[(L["name"], r)])
+        nbw.qgemm_grouped(items, outs=outs)
+    mpg = PeriodGraph(torch, mixed_step, layer.copies)
+    mms = mpg.time(args.steps, args.warmup)
+    del mpg, ymix
+    result["grouped_mixed"] = {"GBps": round(bytes_step / (mms * 1e-3) / 1e9, 1), "ms_per_step": round(mms, 5),
+                               "dispatches_per_step": 1,
+                               "note": "the 12 products (4 linears x r = 4, 3, 2) in one dispatch; independent products"}
+    log(f"batch 1 grouped, one mixed-precision dispatch: {mms * 1e3:.1f} us/step, "
+        f"{result['grouped_mixed']['GBps']} GB/s")
 
     if not args.no_extra:
         # ---- pack (once per checkpoint): 1 byte read + 1 byte written per weight
@@ -550,12 +635,10 @@ def main():
                               out_dtype=kw.get("out_dtype", torch.float32))
         variants = {}
         for name, kw in (("asymmetric", {"asym": True}), ("bf16_out", {"out_dtype": torch.bfloat16})):
-            gr = [capture(torch, lambda j=j, kw=kw: variant_step(j, **kw)) for j in range(layer.copies)]
-            for i in range(5):
-                gr[i % layer.copies].replay()
-            vms = event_time(torch, lambda i: gr[(5 + i) % layer.copies].replay(), max(10, args.steps // 4))
+            vpg = PeriodGraph(torch, lambda j, kw=kw: variant_step(j, **kw), layer.copies)
+            vms = vpg.time(max(10, args.steps // 4), 5)
             variants[name] = {"GBps": round(bytes_step / (vms * 1e-3) / 1e9, 1), "ms_per_step": round(vms, 5)}
-            del gr
+            del vpg
             log(f"batch 1 {name}: {variants[name]['GBps']} GB/s")
         result["variants_b1"] = variants
 
@@ -586,7 +669,7 @@ def main():
                 xb = synth.activations(b, L["k"], synth.rng_for(0, wid, sid, synth.T_X))
                 L[f"x{b}"] = torch.from_numpy(xb).view(torch.bfloat16).cuda()
                 L[f"y{b}"] = torch.empty((b, L["n"]), dtype=torch.float32, device="cuda")
-            stb = Stepper(torch, nbw, layer, RS_B1, f"x{b}", f"y{b}")
+            stb = Stepper(torch, nbw, layer, RS_B1, f"x{b}", f"y{b}", chain=True)
             msb = stb.time(max(10, args.steps // 4), 5, graph=True)
             del stb
             other[f"batch{b}"] = {"GBps": round(bytes_step / (msb * 1e-3) / 1e9, 1),
@@ -685,9 +768,10 @@ def dense_context(torch, layer, result, gen):
         for b in (1, 256):
             x = torch.randn((b, k), device="cuda", generator=gen).to(torch.bfloat16)
             y = torch.empty((b, n), dtype=torch.bfloat16, device="cuda")
-            g = capture(torch, lambda wl=wts, xx=x, yy=y: [torch.mm(xx, wt, out=yy) for wt in wl])
-            g.replay()
-            us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / copies
+            rot = GRAPH_ROTATIONS if b == 1 else 1  # as the sliced products at this batch
+            g = capture(torch, lambda wl=wts, xx=x, yy=y, rot=rot: [torch.mm(xx, wt, out=yy)
+                                                                    for _ in range(rot) for wt in wl])
+            us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / (copies * rot)
             del g
             e = {"linear": L["name"], "batch": b, "dense_us": round(us, 2),
                  "dense_TFLOPs": round(2 * b * n * k / (us * 1e-6) / 1e12, 1)}
@@ -725,14 +809,15 @@ def large_shapes_b1(torch, nbw, gen, kernel="auto"):
         for r in rs:
             calls = [nbw.QgemmCall(x, ws[c].slice_view(r), ss[c], r, out=y, kernel=kernel)
                      for c in range(copies)]
-            g = capture(torch, lambda cl=calls: [c() for c in cl])
+            g = capture(torch, lambda cl=calls: [c() for _ in range(GRAPH_ROTATIONS) for c in cl])
             g.replay()
-            us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / copies
+            us = event_time(torch, lambda i: g.replay(), 3) * 1e3 / (copies * GRAPH_ROTATIONS)
             del g
             bufs = [w.storage for w in ws]
-            gf = capture(torch, lambda bl=bufs: [nbw.stream_read(b, r * pb, sink) for b in bl])
+            gf = capture(torch, lambda bl=bufs: [nbw.stream_read(b, r * pb, sink)
+                                                 for _ in range(GRAPH_ROTATIONS) for b in bl])
             gf.replay()
-            fus = event_time(torch, lambda i: gf.replay(), 3) * 1e3 / copies
+            fus = event_time(torch, lambda i: gf.replay(), 3) * 1e3 / (copies * GRAPH_ROTATIONS)
             del gf
             gbs = r * pb / (us * 1e-6) / 1e9
             out.append({"linear": name, "n": n, "k": k, "r": r, "us": round(us, 2),
