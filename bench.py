@@ -167,14 +167,14 @@ def event_time(torch, body, steps):
     return t0.elapsed_time(t1) / steps
 
 
-# Rotations of the parent copies captured into one graph where a batch-1
+# Rotations of the parent copies captured into one graph where a single
 # product is timed back to back (per-product durations, read floors, the large
-# linears): the gap between graph launches is a visible share of launches of a
-# few us.  Batch-1, -4 and -16 steps likewise run as chains of steps
-# (PeriodGraph).  The large-batch timings keep one graph per step and one
-# rotation per product graph: measured on one box, longer chains of batch-256
-# products ran slower (step 564-570 against 600-607 TFLOP/s).
-GRAPH_ROTATIONS = 4
+# linears, the dense context).  One: measured on one box, graphs of four
+# rotations made the 70B-shaped gate_up at r = 3 20% slower (47.5-49.8 against
+# 39.7-41.5 us) with the same read floor, and batch-256 products ~10% slower.
+# The batch-1, -4 and -16 steps do run as chains of steps (PeriodGraph): there
+# the same-box comparison favoured the chain (86.5-87.2 against 89.0 us).
+GRAPH_ROTATIONS = 1
 
 
 class PeriodGraph:
