@@ -121,11 +121,15 @@ nbw_status nbw_make_view(const void *planes, int64_t n, int64_t k, int32_t nplan
  * r > parent->nplanes. */
 nbw_status nbw_slice_view(const nbw_wview *parent, int32_t r, nbw_wview *child);
 
-/* Y = X . dequant_r(W)^T for the r-bit child of `w` (reads planes 0..r-1
- * only, plus the scales and X).  x_bf16: [batch][k]; scales_bf16:
- * [n][k/128]; y: fp32 [batch][n], fully written.  batch == 0 is an empty
- * product: NBW_OK, nothing queued, x/scales/y unused.  The kernel is chosen
- * by batch size.  Runs on `stream`. */
+/* Y = X . dequant_r(W)^T for the r-bit child of `w` (MatGPTQ: Efficient and
+ * Accurate Inference over Nested Quantized Models, Abstract: an r-bit model
+ * reads exactly r bits, and the kernels serve batch sizes beyond one; Table 1,
+ * row "Exact r-bit loading").  Reads planes 0..r-1 only, plus the scales and
+ * X.  x_bf16: [batch][k]; scales_bf16: [n][k/128]; y: fp32 [batch][n], fully
+ * written.  batch == 0 is an empty product: NBW_OK, nothing queued,
+ * x/scales/y unused.  The kernel is chosen by batch size.  No workspace is
+ * used, so a large-batch launch runs unsplit; Y is deterministic (the same
+ * inputs give bit-identical Y).  Allocates nothing.  Runs on `stream`. */
 nbw_status nbw_qgemm(const void *x_bf16, int64_t batch, const nbw_wview *w,
                      const void *scales_bf16, int32_t r, float *y, void *stream);
 
@@ -161,12 +165,13 @@ typedef struct nbw_qgemm_opts {
                            aligned) of workspace_bytes bytes; no initial
                            contents are needed.  When it holds at least
                            nbw_qgemm_workspace_bytes(...) bytes, a large-batch
-                           launch that splits k meets its splits there: each
-                           split stores its fp32 partial tile and a second
-                           launch on the same stream adds them in a fixed order
-                           (deterministic, fp32 or bf16 Y).  Without it such a
-                           launch clears Y and adds fp32 partial sums with
-                           atomics (fp32 Y only; bf16 Y then runs unsplit).
+                           launch whose output tiles leave compute units idle
+                           splits k and meets its splits there: each split
+                           stores its fp32 partial tile and a second launch on
+                           the same stream adds them in a fixed order.
+                           Without it (NULL or too small) the launch runs
+                           unsplit.  Either way the result is deterministic:
+                           the same inputs give bit-identical Y on every call.
                            Calls that overlap in time must not share a
                            workspace. */
     int64_t workspace_bytes;
@@ -193,8 +198,8 @@ nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
  * with group scale s[i][j/128] (device bf16 [n][k/128]), the code c in 0..255
  * minimising sum_t lambdas[t] * (w - dequant_{widths[t]}(c))^2 over the
  * children r = widths[t] (symmetric closed form above); the first code with
- * the smallest loss wins (MatGPTQ v2, Section 3: per-precision weights
- * lambda_r; MatGPTQ v1 abstract: one parent serves every sliced width).  Every
+ * the smallest loss wins (MatGPTQ v2, captions of Tables 6 and 7: per-precision
+ * weights lambda_r; MatGPTQ v1 abstract: one parent serves every sliced width).  Every
  * code is tried in IEEE double, one rounded operation at a time.  widths and
  * lambdas are HOST arrays of nw (1..8) entries; widths in 1..8, lambdas >= 0
  * and finite.  codes_out: device uint8 [n][k] (ready for nbw_pack_bitplanes).
@@ -226,8 +231,14 @@ typedef struct nbw_problem {
 nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *stream);
 
 /* Child codes q_r = c >> (8 - r) read back from planes 0..r-1 of `w`, through
- * the same in-register plane decode the qgemm kernels use.  codes_out: device
- * uint8 [n][k].  A test hook for the bit-exact slicing check. */
+ * the same in-register plane decode the qgemm kernels use (MatGPTQ: Accurate
+ * and Efficient Post-Training Matryoshka Quantization, abstract: a lower
+ * precision is the parent's most significant bits; MatGPTQ: Efficient and
+ * Accurate Inference over Nested Quantized Models, Abstract: reading fewer
+ * bits of the weights).  codes_out: device uint8 [n][k], fully written.  A
+ * test hook for the bit-exact slicing check.  Errors: NBW_EINVAL (null
+ * pointer or bad view), NBW_ERANGE (r outside 1..w->nplanes), NBW_EALIGN
+ * (codes_out not 16-byte aligned), NBW_EHIP.  Runs on `stream`. */
 nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, void *stream);
 
 /* Bandwidth reference for the batch-1 products (MatGPTQ: Efficient and

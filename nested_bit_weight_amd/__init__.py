@@ -259,7 +259,7 @@ def qgemm(x: torch.Tensor, w: PackedWeight, scales: torch.Tensor, r: int,
     tensor), as may ``out``; ``zeros`` (bf16 [n][k/128]) selects asymmetric
     children; ``out_dtype`` is torch.float32 or torch.bfloat16.  ``workspace``:
     "auto" (the binding's buffer for this device and stream), a uint8 device
-    tensor, or None (split k through fp32 atomics)."""
+    tensor, or None (a large-batch launch then runs unsplit)."""
     _need(scales, "scales", torch.bfloat16, 2)
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-d tensor")
@@ -356,7 +356,8 @@ class QgemmCall:
     kept alive by the object.  Use it where per-call Python cost matters, e.g. when a
     decode step is captured into a HIP graph or launched in a tight loop."""
 
-    __slots__ = ("x", "w", "scales", "r", "out", "kernel", "_args", "_fn", "_dev", "_ws", "_opts")
+    __slots__ = ("x", "w", "scales", "r", "out", "kernel", "_args", "_fn", "_dev", "_nb", "_ws",
+                 "_opts", "_view")
 
     def __init__(self, x, w, scales, r, out=None, kernel="auto"):
         _need(x, "x", torch.bfloat16, 2)
@@ -378,21 +379,31 @@ class QgemmCall:
             raise ValueError(f"unknown kernel {kernel!r}")
         self.x, self.w, self.scales, self.r, self.out, self.kernel = x, w, scales, r, out, kernel
         self._dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
-        nb = workspace_bytes(b, w.n, w.k, r, kernel)
-        self._ws = _workspace(self._dev, _raw_stream(self._dev), nb)
-        self._opts = QgemmOpts(0, 0, 0, KERNELS[kernel], None,
-                               self._ws.data_ptr() if self._ws is not None else None,
-                               self._ws.numel() if self._ws is not None else 0)
-        view = WView.from_buffer_copy(w.view)  # byref() below keeps it alive
-        self._args = (ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(view),
-                      ctypes.c_void_p(scales.data_ptr()), r, ctypes.c_void_p(out.data_ptr()),
-                      ctypes.byref(self._opts))
+        # split-k workspace: the binding's buffer of the stream each call runs on
+        # (calls on one stream never overlap; calls on two streams never share one)
+        self._nb = workspace_bytes(b, w.n, w.k, r, kernel)
+        self._ws = {}
+        self._opts = {}
+        self._view = WView.from_buffer_copy(w.view)
+        self._args = (ctypes.c_void_p(x.data_ptr()), b, ctypes.byref(self._view),
+                      ctypes.c_void_p(scales.data_ptr()), r, ctypes.c_void_p(out.data_ptr()))
         self._fn = _lib().nbw_qgemm_ex
+
+    def _opts_for(self, stream: int):
+        opts = self._opts.get(stream)
+        if opts is None:
+            ws = _workspace(self._dev, stream, self._nb)
+            opts = QgemmOpts(0, 0, 0, KERNELS[self.kernel], None,
+                             ws.data_ptr() if ws is not None else None,
+                             ws.numel() if ws is not None else 0)
+            self._ws[stream] = ws  # keeps the buffer alive with the prepared call
+            self._opts[stream] = opts
+        return opts
 
     def __call__(self, stream=None):
         if stream is None:
             stream = _raw_stream(self._dev)
-        st = self._fn(*self._args, ctypes.c_void_p(stream))
+        st = self._fn(*self._args, ctypes.byref(self._opts_for(stream)), ctypes.c_void_p(stream))
         if st != 0:
             raise NBWError(st, "nbw_qgemm")
         return self.out

@@ -4,8 +4,8 @@
 // minimising the weighted squared error of the children it serves (MatGPTQ:
 // Accurate and Efficient Post-Training Matryoshka Quantization, abstract: one
 // parent, several precisions by slicing the most significant bits; MatGPTQ:
-// Efficient and Accurate Inference over Nested Quantized Models, Section 3:
-// per-precision weights lambda_r):
+// Efficient and Accurate Inference over Nested Quantized Models, captions of
+// Tables 6 and 7: per-precision weights lambda_r):
 //     loss(c) = sum_t lambda_t * (w - s * 2^(8-r_t) * ((c >> (8-r_t)) + 1/2 - 2^(r_t-1)))^2,
 // the first code with the smallest loss winning.  The kernel tries every code
 // (256 per weight, one weight per thread) in IEEE double, one rounded

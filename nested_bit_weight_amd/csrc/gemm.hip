@@ -63,21 +63,17 @@ constexpr int GEMM_TILE = GEMM_BM * GEMM_BN;  // fp32 values of one partial tile
 
 // Stores one 32 x 32 accumulator block: the lane of half h and weight row
 // nrow holds batch rows brow + 8(v/4) + 4h + v%4 (v = 0..15) of column nrow,
-// each scaled by post; added with fp32 atomics or stored (fp32 or bf16).
+// each scaled by post (fp32 or bf16).
 __device__ __forceinline__ void gemm_store_block(const f32x16_t &a, int brow, int h, int nrow,
                                                  int n, int batch, float post, float *y,
-                                                 int64_t ldy, int ybf16, int atomic) {
+                                                 int64_t ldy, int ybf16) {
     if (nrow >= n) return;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int b = brow + 8 * (v >> 2) + 4 * h + (v & 3);
         if (b >= batch) continue;
         const int64_t idx = (int64_t)b * ldy + nrow;
-        const float val = a[v] * post;
-        if (atomic)
-            __hip_atomic_fetch_add(y + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
-            store_y(y, ybf16, idx, val);
+        store_y(y, ybf16, idx, a[v] * post);
     }
 }
 
@@ -110,10 +106,9 @@ template <int R> struct GemmOperand {
 };
 
 // grid: (ceil(n / 256), ceil(batch / 128), splits); block 512.  Groups
-// [z * gps, min(G, (z + 1) * gps)) of k.  Split k (splits > 1) either adds
-// fp32 partial sums into y with atomics (atomic != 0; the launcher has
-// cleared y), or, with a workspace (part != null), stores each split's partial
-// tile there for gemm_reduce_kernel to add in a fixed order.  ASYM:
+// [z * gps, min(G, (z + 1) * gps)) of k.  Split k (splits > 1) needs a
+// workspace (part != null): each split stores its partial tile there for
+// gemm_reduce_kernel to add in a fixed order.  ASYM:
 // asymmetric children, zeros bf16 [n][k/128]: each weight gains
 // s * (127.5 - z) over the symmetric child, i.e. the product gains
 // s * (127.5 - z) * (group sum of the batch row's X), added through the same
@@ -123,7 +118,7 @@ template <int R, bool ASYM>
 __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int batch, const uint8_t *__restrict__ planes,
     int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    int n, int k, int gps, float *__restrict__ y, int64_t ldy, int ybf16, int atomic,
+    int n, int k, int gps, float *__restrict__ y, int64_t ldy, int ybf16,
     float *__restrict__ part) {
     __shared__ __align__(16) uint16_t xs[2][GEMM_BM * GEMM_XSTRIDE];
     // corrections (and group sums of X) of the last four groups, per batch row:
@@ -362,7 +357,7 @@ __global__ __launch_bounds__(64 * GEMM_WAVES) void gemm_kernel(
     // Epilogue: lane holds rows b0 + 32bb + 8(v/4) + 4h + v%4 of column nrow.
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb)
-        gemm_store_block(acc[bb], b0 + 32 * bb, h, nrow, n, batch, POST, y, ldy, ybf16, atomic);
+        gemm_store_block(acc[bb], b0 + 32 * bb, h, nrow, n, batch, POST, y, ldy, ybf16);
 }
 
 // Adds the S partial tiles of a split launch in the order z = 0..S-1 and
@@ -410,22 +405,11 @@ __global__ __launch_bounds__(64) void gemm_reduce_kernel(const float *__restrict
     }
     const int nrow = blockIdx.x * GEMM_BN + 32 * w + (lane & 31);
     gemm_store_block(tot, blockIdx.y * GEMM_BM + 32 * bb, lane >> 5, nrow, n, batch, post, y, ldy,
-                     ybf16, 0);
-}
-
-// Clears the fp32 rows y[b][0..n) (row stride ldy) before a split-k launch
-// adds its partial sums.
-__global__ void gemm_zero_kernel(float *__restrict__ y, int64_t batch, int n, int64_t ldy) {
-    const int64_t count = batch * (int64_t)n;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = i; e < count; e += stride) y[(e / n) * ldy + e % n] = 0.f;
+                     ybf16);
 }
 
 // Split k only when the output tiles leave most CUs idle.  Each split keeps
-// at least min_groups groups: 8 when the splits meet through fp32 atomics
-// (measured at batch 256: below that the atomic adds of the partial tiles
-// outweigh the CUs gained), 4 when they meet in a workspace.
+// at least min_groups groups.
 static int gemm_tiles(const QgemmArgs &a) {
     return (a.n + GEMM_BN - 1) / GEMM_BN * (int)((a.batch + GEMM_BM - 1) / GEMM_BM);
 }
@@ -439,7 +423,6 @@ static int gemm_splits(const QgemmArgs &a, int cu_count, int min_groups) {
 }
 
 constexpr int GEMM_WS_MIN_GROUPS = 4;
-constexpr int GEMM_ATOMIC_MIN_GROUPS = 8;
 
 // Splits that hold at least one group when each takes ceil(G / splits).
 static int gemm_live_splits(int G, int splits) {
@@ -457,32 +440,24 @@ int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count) {
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int G = a.k / 128;
-    // With a large enough workspace the splits meet there (deterministic, any
-    // output type); without one they add fp32 partial sums into y (fp32 only).
+    // The splits meet only in a large enough caller workspace (a fixed order,
+    // so the result is deterministic); without one the launch runs unsplit.
     const int64_t need = gemm_workspace_bytes(a, cu_count);
     const bool use_ws = need > 0 && a.ws && a.ws_bytes >= need;
-    const int want = use_ws ? gemm_splits(a, cu_count, GEMM_WS_MIN_GROUPS)
-                            : (a.ybf16 ? 1 : gemm_splits(a, cu_count, GEMM_ATOMIC_MIN_GROUPS));
+    const int want = use_ws ? gemm_splits(a, cu_count, GEMM_WS_MIN_GROUPS) : 1;
     const int gps = (G + want - 1) / want;
     const int splits = gemm_live_splits(G, want);
     float *part = use_ws ? static_cast<float *>(a.ws) : nullptr;
-    const int atomic = splits > 1 && !use_ws ? 1 : 0;
-    if (atomic) {
-        const int64_t count = a.batch * (int64_t)a.n;
-        const int64_t blocks = (count + 255) / 256;
-        hipLaunchKernelGGL(gemm_zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
-                           dim3(256), 0, stream, a.y, a.batch, a.n, a.ldy);
-    }
     const dim3 grid((a.n + GEMM_BN - 1) / GEMM_BN, (unsigned)((a.batch + GEMM_BM - 1) / GEMM_BM),
                     splits);
     if (a.zeros)
         hipLaunchKernelGGL((gemm_kernel<R, true>), grid, dim3(GEMM_THREADS), 0, stream, a.x,
                            a.ldx, (int)a.batch, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k,
-                           gps, a.y, a.ldy, a.ybf16, atomic, part);
+                           gps, a.y, a.ldy, a.ybf16, part);
     else
         hipLaunchKernelGGL((gemm_kernel<R, false>), grid, dim3(GEMM_THREADS), 0, stream, a.x,
                            a.ldx, (int)a.batch, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k,
-                           gps, a.y, a.ldy, a.ybf16, atomic, part);
+                           gps, a.y, a.ldy, a.ybf16, part);
     if (part)
         hipLaunchKernelGGL(gemm_reduce_kernel, dim3(grid.x, grid.y, 4 * GEMM_WAVES), dim3(64), 0,
                            stream, part, splits, (int)a.batch, a.n, GemmOperand<R>::post, a.y,

@@ -253,8 +253,9 @@ int nbwo_qgemm_asym_rows(const uint16_t *x, int64_t batch, const uint8_t *planes
  * c in [0, 255] that minimises the weighted squared error of the children it
  * serves (MatGPTQ: Accurate and Efficient Post-Training Matryoshka
  * Quantization, abstract: one parent serves several precisions; MatGPTQ:
- * Efficient and Accurate Inference over Nested Quantized Models, Section 3
- * on the per-precision weights lambda_3, lambda_4, lambda_8):
+ * Efficient and Accurate Inference over Nested Quantized Models, captions of
+ * Tables 6 and 7, which name the per-precision weights lambda_3, lambda_4,
+ * lambda_8):
  *     loss(c) = sum_t lambda_t * (w - dequant(s, c >> (8 - r_t), r_t))^2,
  * for the widths r_t in `widths` (nw of them).  Every code is tried in order
  * 0..255; the first code with the smallest loss wins.  All arithmetic is

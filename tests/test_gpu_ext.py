@@ -107,13 +107,9 @@ def test_bf16_output(nbw, kernel, batch, r):
     assert y16.dtype == torch.bfloat16
     got = y16.float().cpu().numpy().astype(np.float64)
     f32 = y32.cpu().numpy()
-    if kernel == "gemm":
-        # the fp32 launch may split k (atomic partial sums) where the bf16 one
-        # does not: same value up to fp32 rounding, so within one bf16 rounding
-        assert np.all(np.abs(got - f32) <= 2.0 ** -8 * np.abs(f32) + 1e-6 * np.abs(f32).max())
-    else:
-        # exactly the fp32 result rounded to nearest even
-        assert np.array_equal(got, bf16_round(f32))
+    # exactly the fp32 result rounded to nearest even (both launches take the
+    # same path and summation order)
+    assert np.array_equal(got, bf16_round(f32))
     ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, r)
     bound = 2.0 ** -8 * np.abs(ref) + CONTRACT * np.abs(ref).max(axis=1, keepdims=True)
     assert np.all(np.abs(got - ref) <= bound)

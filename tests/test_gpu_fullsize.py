@@ -1,13 +1,19 @@
-"""GPU parity at the workloads' full sizes, beyond the Llama-3.1-8B layer.
+"""GPU parity at the workloads' full sizes.
 
 * the single 1024 x 1024 linear (uniform parent codes, scales U(0.001, 0.01),
   X ~ N(0, 1), batch 1, r = 8, 4, 2): every output against the fp64 oracle,
   on every kernel;
-* the Qwen3-8B-shaped linears (batch 1, 4, 32, 64, 256; r = 6, 4, 3, 2) and the
-  70B-shaped layer (batch 1, 16, 128; r = 3, 2) at full size, through the
-  automatic kernel choice (the launch configuration the bench times): the
-  output rows of the first and last tiles plus 59 seeded rows against the
-  oracle, which packs those rows' codes itself.
+* every (shape, batch, r) the bench times, at full size, through the automatic
+  kernel choice (the launch configuration the bench times), on the bench's
+  own inputs (the same seeded generator calls, X per batch: no outlier
+  channels at batch <= 16, 1% outlier channels x10 from batch 32):
+  - the Llama-3.1-8B linears at batch 1, 4, 16 (r = 4, 3, 2) and batch 32,
+    64, 128, 256 (r = 8, 4, 3, 2);
+  - the Qwen3-8B-shaped linears over the batch sweep 1, 2, 4, ..., 256
+    (r = 6, 4, 3, 2);
+  - the 70B-shaped layer at batch 1, 16, 128 (r = 3, 2);
+  checked on the output rows of the first and last tiles plus 59 seeded rows
+  against the oracle, which packs those rows' codes itself.
 
 Bars as in test_gpu_parity: max |Y - R| / max |R| per batch row <= 2e-3 (the
 contract) and <= 1e-4 (exact bf16 operands, fp32 accumulation).
@@ -62,12 +68,21 @@ def test_single_1024_every_output(nbw, kernel):
 
 
 @functools.lru_cache(maxsize=1)
-def _layer(workload, shape_id, batch):
-    return synth.make_linear(workload, shape_id, batch)
+def _weights(workload, shape_id):
+    return synth.make_linear(workload, shape_id, 1)
 
 
-def _sampled(nbw, workload, shape_id, batches, rs):
-    d = _layer(workload, shape_id, max(batches))
+def _x(workload, shape_id, k, batch):
+    """The bench's activations for this linear and batch (outliers from batch 32)."""
+    wid = synth.WORKLOAD_IDS[workload]
+    return synth.activations(batch, k, synth.rng_for(0, wid, shape_id, synth.T_X),
+                             outliers=batch >= 32,
+                             outlier_rng=synth.rng_for(0, wid, shape_id, synth.T_OUTLIERS))
+
+
+def _sampled(nbw, workload, shape_id, plan):
+    """plan: sequence of (batch, widths)."""
+    d = _weights(workload, shape_id)
     n, k = d["n"], d["k"]
     rng = np.random.default_rng(1000 + shape_id)
     rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n), rng.integers(0, n, 59)]))
@@ -75,8 +90,8 @@ def _sampled(nbw, workload, shape_id, batches, rs):
     sub_scales = np.ascontiguousarray(d["scales"][rows])
     w = nbw.pack_bitplanes(dev(d["codes"]))
     s = dev(d["scales"], torch.bfloat16)
-    for b in batches:
-        xb = np.ascontiguousarray(d["x"][:b])
+    for b, rs in plan:
+        xb = _x(workload, shape_id, k, b)
         x = dev(xb, torch.bfloat16)
         for r in rs:
             print(f"{workload} {d['name']} b={b} r={r} kernel={nbw.kernel_name(b, n, k, r)}", flush=True)
@@ -88,11 +103,22 @@ def _sampled(nbw, workload, shape_id, batches, rs):
             assert e <= CONTRACT and e <= DESIGN_BOUND
 
 
+LLAMA_PLAN = [(1, (4, 3, 2)), (4, (4, 3, 2)), (16, (4, 3, 2)),
+              (32, (8, 4, 3, 2)), (64, (8, 4, 3, 2)), (128, (8, 4, 3, 2)), (256, (8, 4, 3, 2))]
+QWEN_PLAN = [(b, (6, 4, 3, 2)) for b in (1, 2, 4, 8, 16, 32, 64, 128, 256)]
+L70_PLAN = [(b, (3, 2)) for b in (1, 16, 128)]
+
+
+@pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
+def test_llama31_8b_full_size_sampled(nbw, shape_id):
+    _sampled(nbw, "llama3.1-8b", shape_id, LLAMA_PLAN)
+
+
 @pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
 def test_qwen3_8b_full_size_sampled(nbw, shape_id):
-    _sampled(nbw, "qwen3-8b", shape_id, (1, 4, 32, 64, 256), (6, 4, 3, 2))
+    _sampled(nbw, "qwen3-8b", shape_id, QWEN_PLAN)
 
 
 @pytest.mark.parametrize("shape_id", [0, 1, 2, 3])
 def test_llama70b_full_size_sampled(nbw, shape_id):
-    _sampled(nbw, "llama-70b", shape_id, (1, 16, 128), (3, 2))
+    _sampled(nbw, "llama-70b", shape_id, L70_PLAN)

@@ -1,17 +1,21 @@
 """GPU checks of the large-batch GEMM's split-k paths.
 
-When a launch splits k, its splits meet either in a caller workspace (each
-split stores its partial tile, a second launch adds them in the fixed split
-order) or through fp32 atomic adds into Y.  Checked here:
+When a launch splits k, its splits meet in a caller workspace: each split
+stores its partial tile and a second launch adds them in the fixed split
+order.  Without a (large enough) workspace the launch runs unsplit.  Checked
+here:
 
 * the workspace path against the fp64 oracle (fp32 and bf16 Y, symmetric and
   asymmetric children), within the qgemm contract and the fp32 design bound;
 * it is deterministic (two calls bit-identical) and its bf16 Y is exactly its
   fp32 Y rounded to nearest even (same summation order);
-* it agrees with the atomic path up to fp32 rounding;
+* it agrees with the unsplit launch up to fp32 rounding, and the unsplit
+  launch is deterministic too;
 * it needs no initial workspace contents (workspaces start as NaN bytes) and
   a workspace can be reused across calls and shapes;
-* a workspace smaller than required falls back to the atomic path.
+* a workspace smaller than required leaves it untouched and runs unsplit;
+* the plain C entry point nbw_qgemm (no workspace) gives bit-identical Y on
+  two calls at a shape whose large-batch launch would split k.
 """
 import numpy as np
 import pytest
@@ -76,7 +80,9 @@ def test_workspace_split_matches_oracle(nbw, batch, n, k, r):
     y16 = nbw.qgemm(x, nbw.slice_view(w, r), s, r, kernel="gemm", workspace=ws,
                     out_dtype=torch.bfloat16)
     ya = nbw.qgemm(x, nbw.slice_view(w, r), s, r, kernel="gemm", workspace=None)
+    ya2 = nbw.qgemm(x, nbw.slice_view(w, r), s, r, kernel="gemm", workspace=None)
     torch.cuda.synchronize()
+    assert torch.equal(ya, ya2)                                 # unsplit: deterministic too
     ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, r)
     e = rel_err(y.cpu().numpy(), ref)
     print(f"split b={batch} n={n} k={k} r={r} err={e:.3e}", flush=True)
@@ -108,7 +114,7 @@ def test_workspace_reused_across_shapes_and_short_workspace_falls_back(nbw):
             torch.cuda.synchronize()
             ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, 4)
             assert rel_err(y.cpu().numpy(), ref) <= DESIGN_BOUND
-    # too small: the atomic path runs (fp32) and is still right
+    # too small: the launch runs unsplit and is still right
     batch, n, k = SHAPES[0]
     case, w, x, s = _case(nbw, batch, n, k, seed=9)
     small = torch.full((256,), 0x5A, dtype=torch.uint8, device="cuda")
@@ -117,3 +123,28 @@ def test_workspace_reused_across_shapes_and_short_workspace_falls_back(nbw):
     ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, 4)
     assert rel_err(y.cpu().numpy(), ref) <= DESIGN_BOUND
     assert bool((small == 0x5A).all())   # untouched
+
+
+def test_plain_entry_point_is_deterministic(nbw):
+    """nbw_qgemm through the C ABI (no workspace) on the Llama-3.1-8B o shape at
+    batch 256, where a launch with a workspace splits k: two calls, bit-identical Y."""
+    import ctypes
+    batch, n, k, r = 256, 4096, 4096, 4
+    assert nbw.workspace_bytes(batch, n, k, r) > 0, "the shape must be one that splits k"
+    case, w, x, s = _case(nbw, batch, n, k, seed=77)
+    lib = nbw.library()
+    view = nbw.slice_view(w, r).view
+    ys = []
+    for _ in range(2):
+        y = torch.full((batch, n), float("nan"), dtype=torch.float32, device="cuda")
+        st = lib.nbw_qgemm(ctypes.c_void_p(x.data_ptr()), batch, ctypes.byref(view),
+                           ctypes.c_void_p(s.data_ptr()), r, ctypes.c_void_p(y.data_ptr()),
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    rows = np.arange(0, n, 61)
+    ref = oracle.qgemm_rows(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, r, rows)
+    got = ys[0].cpu().numpy()[:, rows].astype(np.float64)
+    assert rel_err(got, ref) <= CONTRACT

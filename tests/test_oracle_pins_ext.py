@@ -9,7 +9,8 @@ bucket mean computed in exact rationals, the reduction to the symmetric
 closed form at z = 127.5, and linearity in z.
 
 Code chooser (MatGPTQ: Efficient and Accurate Inference over Nested Quantized
-Models, Section 3: per-precision weights lambda_3, lambda_4, lambda_8): the
+Models, captions of Tables 6 and 7: per-precision weights lambda_3, lambda_4,
+lambda_8): the
 chosen parent code minimises the lambda-weighted squared error of the
 children; ties go to the smallest code.  Pinned by closed forms for a single
 width, exact power-of-two scale invariance, sign symmetry and an exact
