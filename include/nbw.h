@@ -66,7 +66,9 @@ typedef enum nbw_status {
     NBW_EALIGN = 2,       /* a pointer misses its required alignment */
     NBW_ERANGE = 3,       /* r outside 1..8, or r larger than the planes present */
     NBW_EUNSUPPORTED = 4, /* unknown layout or kernel selector */
-    NBW_EHIP = 5          /* a HIP runtime call failed (see nbw_last_hip_error) */
+    NBW_EHIP = 5,         /* a HIP runtime call failed (see nbw_last_hip_error) */
+    NBW_ESCRATCH = 6      /* nbw_qgemm_noalloc: the problem needs more scratch than
+                             NBW_NOALLOC_SCRATCH_BYTES */
 } nbw_status;
 
 #define NBW_LAYOUT_T16 1
@@ -193,6 +195,29 @@ int64_t nbw_qgemm_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t r
 nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
                         const void *scales_bf16, int32_t r, void *y, const nbw_qgemm_opts *opts,
                         void *stream);
+
+/* Size of the static device scratch behind nbw_qgemm_noalloc (64 MiB per
+ * device that runs it, held until the process ends). */
+#define NBW_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+
+/* nbw_qgemm_ex for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It calls no
+ * hipMalloc, hipFree or other allocating routine.  Where a large-batch launch
+ * splits k, its partial tiles go to a static device scratch array of the
+ * library (NBW_NOALLOC_SCRATCH_BYTES, one per device, its address looked up
+ * once per device on the first call there) instead of a caller workspace;
+ * results are bit-identical to nbw_qgemm_ex given a large enough workspace.
+ * Same arguments and errors as nbw_qgemm_ex, except: opts->workspace must be
+ * NULL and opts->workspace_bytes 0 (NBW_EINVAL otherwise), and a problem
+ * whose split needs more than NBW_NOALLOC_SCRATCH_BYTES
+ * (nbw_qgemm_workspace_bytes) returns NBW_ESCRATCH with nothing queued.  Every
+ * call on a device shares that device's scratch and leaves it holding its
+ * partial tiles (no initial contents are needed): calls that overlap in time
+ * on one device -- on two streams, or from two threads -- race on it and must
+ * be serialised by the caller. */
+nbw_status nbw_qgemm_noalloc(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                             const void *scales_bf16, int32_t r, void *y,
+                             const nbw_qgemm_opts *opts, void *stream);
 
 /* Data-free parent-code choice: for every fp32 weight w[i][j] (device, [n][k])
  * with group scale s[i][j/128] (device bf16 [n][k/128]), the code c in 0..255

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libnbw.so")
 NBW_LAYOUT_T16 = 1
 KERNELS = {"auto": 0, "gemv": 1, "smallb": 2, "gemm": 3}
 _STATUS = {0: "NBW_OK", 1: "NBW_EINVAL", 2: "NBW_EALIGN", 3: "NBW_ERANGE",
-           4: "NBW_EUNSUPPORTED", 5: "NBW_EHIP"}
+           4: "NBW_EUNSUPPORTED", 5: "NBW_EHIP", 6: "NBW_ESCRATCH"}
 
 
 class NBWError(RuntimeError):
@@ -71,7 +71,7 @@ FILE_HEADER_BYTES = 4096
 _LIB = None
 
 EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_make_view",
-           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex",
+           "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex", "nbw_qgemm_noalloc",
            "nbw_qgemm_workspace_bytes", "nbw_qgemm_grouped",
            "nbw_choose_codes", "nbw_unpack_codes", "nbw_stream_sink_words", "nbw_stream_read",
            "nbw_file_prefix_bytes", "nbw_file_header", "nbw_file_parse",
@@ -102,6 +102,8 @@ def _lib():
         lib.nbw_qgemm_kernel.restype = ctypes.c_int
         lib.nbw_qgemm_ex.argtypes = [vp, i64, pv, vp, i32, vp, ctypes.POINTER(QgemmOpts), vp]
         lib.nbw_qgemm_ex.restype = ctypes.c_int
+        lib.nbw_qgemm_noalloc.argtypes = [vp, i64, pv, vp, i32, vp, ctypes.POINTER(QgemmOpts), vp]
+        lib.nbw_qgemm_noalloc.restype = ctypes.c_int
         lib.nbw_choose_codes.argtypes = [vp, i64, i64, vp, ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_double), i32, vp, vp]
         lib.nbw_choose_codes.restype = ctypes.c_int

@@ -10,6 +10,12 @@
 #include "launch.h"
 #include "nbw.h"
 
+// Scratch of nbw_qgemm_noalloc: the split-k partial tiles of a large-batch
+// launch live here instead of in a caller workspace.  One copy per device,
+// held until the process ends; its device address is taken once per device
+// (scratch_ptr below) -- the name itself is a host-side stand-in.
+static __device__ __align__(256) unsigned char scratch[NBW_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
@@ -39,6 +45,27 @@ nbw_status cu_count(int *out) {
         e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_failed(e);
         cache[dev] = v > 0 ? v : 1;
+    }
+    *out = cache[dev];
+    return NBW_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and cached.
+nbw_status scratch_ptr(void **out) {
+    static std::mutex mu;
+    static std::vector<void *> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_failed(e);
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, nullptr);
+    if (!cache[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_failed(e);
+        if (!p) return NBW_EHIP;
+        cache[dev] = p;
     }
     *out = cache[dev];
     return NBW_OK;
@@ -182,6 +209,29 @@ nbw_status nbw_qgemm_ex(const void *x_bf16, int64_t batch, const nbw_wview *w,
     default: e = nbw::launch_gemm(r, a, cus, (hipStream_t)stream); break;
     }
     return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
+nbw_status nbw_qgemm_noalloc(const void *x_bf16, int64_t batch, const nbw_wview *w,
+                             const void *scales_bf16, int32_t r, void *y,
+                             const nbw_qgemm_opts *opts, void *stream) {
+    nbw_qgemm_opts o = {};
+    if (opts) o = *opts;
+    if (o.workspace || o.workspace_bytes) return NBW_EINVAL;  // the scratch replaces it
+    const nbw_status st = check_view(w);
+    if (st != NBW_OK) return st;
+    if (r < 1 || r > 8 || r > w->nplanes) return NBW_ERANGE;
+    if (o.kernel < NBW_KERNEL_AUTO || o.kernel > NBW_KERNEL_GEMM) return NBW_EUNSUPPORTED;
+    const int64_t need = nbw_qgemm_workspace_bytes(batch, w->n, w->k, r, (nbw_kernel)o.kernel);
+    if (need < 0) return NBW_EINVAL;
+    if (need > NBW_NOALLOC_SCRATCH_BYTES) return NBW_ESCRATCH;
+    if (need > 0) {
+        void *p = nullptr;
+        const nbw_status sp = scratch_ptr(&p);
+        if (sp != NBW_OK) return sp;
+        o.workspace = p;
+        o.workspace_bytes = NBW_NOALLOC_SCRATCH_BYTES;
+    }
+    return nbw_qgemm_ex(x_bf16, batch, w, scales_bf16, r, y, &o, stream);
 }
 
 nbw_status nbw_qgemm_kernel(const void *x_bf16, int64_t batch, const nbw_wview *w,
@@ -336,6 +386,7 @@ const char *nbw_status_str(nbw_status s) {
     case NBW_ERANGE: return "bit-width out of range";
     case NBW_EUNSUPPORTED: return "unsupported layout or kernel";
     case NBW_EHIP: return "HIP runtime error";
+    case NBW_ESCRATCH: return "problem needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }

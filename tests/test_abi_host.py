@@ -119,7 +119,7 @@ def test_pack_and_unpack_validation(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.nbw_status_str(s)
     assert b"gfx950" in lib.nbw_version()
     assert lib.nbw_last_hip_error() == 0
@@ -199,3 +199,18 @@ def test_stream_read_validation(lib):
     assert lib.nbw_stream_read(vp(FAKE), 1000, vp(FAKE), None) == EINVAL   # not a multiple of 16
     assert lib.nbw_stream_read(vp(FAKE + 8), 1024, vp(FAKE), None) == EALIGN
     assert lib.nbw_stream_read(vp(FAKE), 1024, vp(FAKE + 2), None) == EALIGN
+
+
+def test_noalloc_rejects_before_any_device_work(lib):
+    p = ctypes.c_void_p
+    _, v = _view(lib)
+    o = nbw.QgemmOpts(0, 0, 0, 0, None, FAKE, 4096)   # a caller workspace is refused
+    assert lib.nbw_qgemm_noalloc(p(FAKE), 4, ctypes.byref(v), p(FAKE), 4, p(FAKE), ctypes.byref(o),
+                                 None) == EINVAL
+    o = nbw.QgemmOpts()
+    assert lib.nbw_qgemm_noalloc(p(FAKE), 4, ctypes.byref(v), p(FAKE), 9, p(FAKE), ctypes.byref(o),
+                                 None) == ERANGE
+    o.kernel = 7
+    assert lib.nbw_qgemm_noalloc(p(FAKE), 4, ctypes.byref(v), p(FAKE), 4, p(FAKE), ctypes.byref(o),
+                                 None) == EUNSUPPORTED
+    assert b"scratch" in lib.nbw_status_str(6)
