@@ -15,8 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnbw.so")
-SOURCES = ["abi.hip", "pack.hip", "gemv.hip", "smallb.hip", "gemm.hip", "choose.hip", "stream.hip",
-           "file.hip"]
+SOURCES = ["abi.hip", "pack.hip", "gemv.hip", "smallb.hip", "gemm.hip", "gemm_wide.hip", "choose.hip",
+           "stream.hip", "file.hip"]
 ARCH = "gfx950"
 
 

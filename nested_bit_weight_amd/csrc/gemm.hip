@@ -430,11 +430,20 @@ static int gemm_live_splits(int G, int splits) {
     return (G + gps - 1) / gps;
 }
 
-// Workspace of the deterministic split: splits x tiles partial tiles of fp32.
-int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count) {
+// Workspace of the deterministic split (splits x tiles partial tiles of
+// fp32) of this kernel, which takes asymmetric children.
+static int64_t gemm_asym_workspace_bytes(const QgemmArgs &a, int cu_count) {
     const int splits = gemm_live_splits(a.k / 128, gemm_splits(a, cu_count, GEMM_WS_MIN_GROUPS));
     if (splits <= 1) return 0;
     return (int64_t)splits * gemm_tiles(a) * GEMM_TILE * 4;
+}
+
+// Workspace that covers either large-batch kernel (symmetric children take
+// gemm_wide_kernel, asymmetric ones this file's kernel).
+int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count) {
+    const int64_t sym = gemm_wide_workspace_bytes(a, cu_count);
+    const int64_t asym = gemm_asym_workspace_bytes(a, cu_count);
+    return sym > asym ? sym : asym;
 }
 
 template <int R>
@@ -442,7 +451,7 @@ static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int G = a.k / 128;
     // The splits meet only in a large enough caller workspace (a fixed order,
     // so the result is deterministic); without one the launch runs unsplit.
-    const int64_t need = gemm_workspace_bytes(a, cu_count);
+    const int64_t need = gemm_asym_workspace_bytes(a, cu_count);
     const bool use_ws = need > 0 && a.ws && a.ws_bytes >= need;
     const int want = use_ws ? gemm_splits(a, cu_count, GEMM_WS_MIN_GROUPS) : 1;
     const int gps = (G + want - 1) / want;
@@ -465,6 +474,7 @@ static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
 }
 
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {
+    if (!a.zeros) return launch_gemm_wide(r, a, cu_count, stream);
     switch (r) {
     case 1: launch_r<1>(a, cu_count, stream); break;
     case 2: launch_r<2>(a, cu_count, stream); break;
@@ -481,7 +491,10 @@ hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stre
 
 void gemm_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
     (void)cu_count;
-    snprintf(out, len, "nbw::gemm_kernel<%d, %s>", r, a.zeros ? "true" : "false");
+    if (!a.zeros)
+        gemm_wide_name(r, a, out, len);
+    else
+        snprintf(out, len, "nbw::gemm_kernel<%d, true>", r);
 }
 
 }  // namespace nbw

@@ -53,6 +53,11 @@ hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t st
 // Batch rows the small-batch kernel covers per pass over the planes (16 or 32).
 int smallb_pass_rows(int r, int n, int cu_count);
 hipError_t launch_gemm(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
+// The large-batch kernel of symmetric children (gemm_wide.hip) and its split-k
+// workspace bytes (0: the launch does not split).
+hipError_t launch_gemm_wide(int r, const QgemmArgs &a, int cu_count, hipStream_t stream);
+int64_t gemm_wide_workspace_bytes(const QgemmArgs &a, int cu_count);
+void gemm_wide_name(int r, const QgemmArgs &a, char *out, size_t len);
 // Workspace bytes the large-batch GEMM uses to split k deterministically (0:
 // the launch does not split).
 int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count);

@@ -88,7 +88,17 @@ def test_asym_midpoint_zero_equals_symmetric_bitwise(nbw, kernel, r):
     ya = nbw.qgemm(x, nbw.slice_view(w, r), s, r, kernel=kernel, zeros=dev(half, torch.bfloat16))
     ys = nbw.qgemm(x, nbw.slice_view(w, r), s, r, kernel=kernel)
     torch.cuda.synchronize()
-    assert torch.equal(ya, ys)
+    if kernel != "gemm":
+        # the same kernel with the zero-point term switched on: bit-identical
+        assert torch.equal(ya, ys)
+    else:
+        # at large batch symmetric children run on their own kernel (the
+        # asymmetric ones on the zero-point variant), so the two sum in
+        # different orders: equal up to fp32 rounding, and each within the
+        # design bound of the oracle
+        ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], n, k, r)
+        assert rel_err(ya.cpu().numpy(), ys.cpu().numpy().astype(np.float64)) <= 1e-5
+        assert rel_err(ya.cpu().numpy(), ref) <= 1e-4 and rel_err(ys.cpu().numpy(), ref) <= 1e-4
 
 
 # ---------------------------------------------------------------- bf16 output

@@ -203,7 +203,17 @@ def test_metamorphic_scale_and_sign(nbw, kernel):
     c2 = dict(case, scales=case["scales"] + np.uint16(1 << 7))     # scales x 2
     np.testing.assert_array_equal(run_qgemm(nbw, c2, 4, kernel), 2 * y)
     cn = dict(case, x=case["x"] ^ np.uint16(0x8000))                # X -> -X
-    np.testing.assert_array_equal(run_qgemm(nbw, cn, 4, kernel), -y)
+    yn = run_qgemm(nbw, cn, 4, kernel)
+    if kernel != "gemm":
+        np.testing.assert_array_equal(yn, -y)
+    else:
+        # The large-batch kernel adds its offset corrections to the running
+        # sums on the matrix unit, whose accumulation of products of unlike
+        # magnitude is not rounded to nearest and not odd in its inputs
+        # (measured on gfx950: negated inputs give a result that is not the
+        # negated one in 0.2% to 30% of outputs, by up to an ulp of the
+        # running sum).  X -> -X then holds to fp32 rounding only.
+        assert rel_err(yn, -y.astype(np.float64)) <= 1e-5
     np.testing.assert_array_equal(run_qgemm(nbw, case, 4, kernel), y)  # run twice
 
 

