@@ -21,13 +21,14 @@
 //  - each wave walks its (set, tile) steps as one stream with PD steps of
 //    planes and scales in flight; all loads are unconditional (clamped at the
 //    end), so the loads-in-flight count between a load and its use is static.
-//  - the activations and the per-group offset corrections are staged in LDS
-//    once per workgroup; a set switch reloads the lane's 64 bf16 activation
-//    pairs from LDS without touching the memory pipeline.
+//  - the activations are staged in LDS by each wave for its set; a set switch
+//    reloads the lane's MFMA operand from LDS without touching the memory
+//    pipeline.
 //  - decode: bit-plane transpose network + one shift / and-or per bf16 pair
-//    (decode.h), then v_dot2_f32_bf16; the group scale is folded in fp32 once
-//    per (row, group); the four groups of a set meet through two cross-lane
-//    exchanges and the waves in LDS, in a fixed order.
+//    (decode.h) on the VALU; the products on the matrix cores, with a block
+//    diagonal activation operand that keeps the set's four groups in four
+//    output rows (see gemv_tiles); the group scales are folded in fp32 once
+//    per (row, group), and the waves meet in LDS in a fixed order.
 #include <cstdio>
 
 #include "decode.h"
@@ -35,10 +36,16 @@
 
 namespace nbw {
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 constexpr int GEMV_MAX_WAVES = 8;   // waves per workgroup (the launch picks 4 or 8)
 constexpr int GEMV_ODD_WAVES = 4;   // waves per workgroup of the odd-group-count kernel
 constexpr int GEMV_MAX_TILES = 16;  // tiles per workgroup
 constexpr int GEMV_MAX_GROUP = 32;  // products per grouped launch
+// Workgroups per CU the launch plans for.  (Measured on 70B- and
+// Llama-3.1-8B-sized linears: two workgroups per CU, with the MFMA operand
+// read from LDS to fit the registers, were 5-15% slower than one.)
+constexpr int GEMV_WGS_PER_CU = 1;
 
 // Steps a wave keeps in flight (prefetch depth).  Every wave of the grid
 // prefetches this many steps at once, so the total in flight must stay near
@@ -50,10 +57,12 @@ constexpr int GEMV_MAX_GROUP = 32;  // products per grouped launch
 constexpr int GEMV_DEPTH_SHORT = 1;
 __host__ __device__ constexpr int gemv_depth(int r) { return r <= 6 ? 2 : 1; }
 
-// Dynamic LDS: per wave, one set of X (4 groups x 128 bf16 = 1 KB), then the
-// per-lane partial sums fp32 [W][slots][64], one slot per tile.
+// Dynamic LDS: per wave, one set of X (4 groups x 128 bf16 = 1 KB) and 256
+// bytes of zeros, then the per-row partial sums fp32 [W][slots][16], one slot
+// per tile.
+constexpr int GEMV_WAVE_LDS = 1024 + 256;
 __host__ __device__ constexpr size_t gemv_lds_bytes(int waves, int slots) {
-    return (size_t)waves * 1024 + (size_t)waves * slots * 64 * 4;
+    return (size_t)waves * GEMV_WAVE_LDS + (size_t)waves * slots * 16 * 4;
 }
 
 // Sum over each 16-lane row of the wave, in every lane of the row: DPP quad
@@ -73,13 +82,29 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // One workgroup: tiles [t_begin, t_begin + T) of one product, all of k;
-// `slots` partial-sum slots per wave in LDS (T <= slots).
+// `slots` partial-sum slots per wave in LDS (T <= slots).  k/128 is a
+// multiple of 4: a set is four whole groups.
+//
+// The dot products run on the matrix cores, the decode on the VALU.  One
+// v_mfma_f32_16x16x32_bf16 takes 32 columns: lane (i, h) of the wave (i =
+// lane % 16, h = lane / 16) supplies 8 decoded weights of row i, group
+// 4*set + h (B operand) and, as row i of the A operand, the same 8 columns
+// of X if i == h and zeros otherwise.  A is block diagonal, so output row v
+// holds group 4*set + v alone: after the 16 MFMAs of a step (4 words x 4
+// pair quads), lane i holds row i's four group sums in its four accumulator
+// registers, and scales them there.  The 15 zero rows of A are the price of
+// batch 1; the matrix cores are otherwise idle, and the VALU keeps only the
+// decode.
 //
 // Waves are independent until the final reduction: a wave loads the X of its
 // current set itself (one 16-byte load per lane, part of the step's load
-// stream), stages it in its own 1 KB of LDS and reads back its lanes'
-// groups, so no barrier -- and no wait for every load in flight -- stands
+// stream), stages it in its own 1 KB of LDS and reads back its lanes' A
+// operands, so no barrier -- and no wait for every load in flight -- stands
 // between a wave's first loads and its first step.
 template <int R, int PD, bool ASYM>
 __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
@@ -89,14 +114,16 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
                                            const uint16_t *__restrict__ zeros, int n, int k,
                                            int t_begin, int T, int slots, float *__restrict__ y,
                                            int ybf16, unsigned char *lds) {
+    constexpr int NPH = Phases<R>::count;
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
     const int W = blockDim.x >> 6;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int i = lane & 15, gg = lane >> 4;
-    uint32_t *xw = reinterpret_cast<uint32_t *>(lds) + w * 256;          // this wave's set of X
-    float *red = reinterpret_cast<float *>(lds + (size_t)W * 1024);      // [W][slots][64]
+    uint32_t *xw = reinterpret_cast<uint32_t *>(lds + (size_t)w * GEMV_WAVE_LDS);  // this wave's set of X
+    uint32_t *zblk = xw + 256;                                                      // 256 B of zeros
+    float *red = reinterpret_cast<float *>(lds + (size_t)W * GEMV_WAVE_LDS);        // [W][slots][16]
 
     // This wave's (set, tile) steps: set ordinal s = 0 .. my_sets-1 is set
     // w + s*W, tile t = 0 .. T-1; step u = s*T + t.
@@ -104,8 +131,10 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     const int U = my_sets * T;
 
     // Zero this wave's partial sums (only this wave writes them until the
-    // final barrier).
-    for (int t = 0; t < T; ++t) red[(w * slots + t) * 64 + lane] = 0.f;
+    // final barrier) and its zero block.
+    zblk[lane] = 0u;
+    if (gg == 0)
+        for (int t = 0; t < T; ++t) red[(w * slots + t) * 16 + i] = 0.f;
 
     // Coefficient of this lane's pair sums in the group correction
     // sum_k x_k * (1/2 - 2^(R-1) - offset_k): lane (i, gg) takes the pairs
@@ -115,15 +144,16 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     for (int m = 0; m < 16; ++m)
         if (i == m) my_coef = pair_coef<R>(m);
 
-    // Step loads: R plane chunks, the aligned 32-bit scale word, and the
+    // Step loads: R plane chunks (row i, group 4*set + gg), the two aligned
+    // 32-bit words of the scales of row i's four groups of the set, and the
     // lane's 16 bytes of the set's X (the same chunk for every tile of a set;
     // reloading it keeps the number of loads per step fixed).  All loads are
-    // unconditional (clamped at the end), so the loads-in-flight count between
-    // a load and its use is static.
+    // unconditional (clamped at the end), so the loads-in-flight count
+    // between a load and its use is static.
     u32x4_t buf[PD][R];
     u32x4_t xbuf[PD];
-    uint32_t sbuf[PD];
-    uint32_t zbuf[ASYM ? PD : 1];
+    u32x2_t sbuf[PD];
+    u32x2_t zbuf[ASYM ? PD : 1];
     int ps = 0, pt = 0;  // next step to prefetch
     const int xchunks = k >> 3;
     auto load_step = [&](int j) {
@@ -140,13 +170,12 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         for (int p = 0; p < R; ++p)
             buf[j][p] =
                 __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(c + p * plane_bytes));
-        // (in bounds: the host sends only even group counts here; a 16-bit
-        // load would need a zero-extension that the compiler may place where
-        // it waits for every load in flight)
+        // groups 4*set .. 4*set+3 of row i: one aligned 8-byte word (k/128 is
+        // a multiple of 4)
         const int row = min(16 * (t_begin + t) + i, n - 1);
-        const int64_t idx = (int64_t)row * G + g;
-        sbuf[j] = *reinterpret_cast<const uint32_t *>(scales + (idx & ~(int64_t)1));
-        if constexpr (ASYM) zbuf[j] = *reinterpret_cast<const uint32_t *>(zeros + (idx & ~(int64_t)1));
+        const int64_t r0 = (int64_t)row * G + 4 * set;
+        sbuf[j] = *reinterpret_cast<const u32x2_t *>(scales + r0);
+        if constexpr (ASYM) zbuf[j] = *reinterpret_cast<const u32x2_t *>(zeros + r0);
         if (++pt == T) {
             pt = 0;
             ++ps;
@@ -157,32 +186,38 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         for (int j = 0; j < PD; ++j) load_step(j);
     }
 
-    uint32_t X2[64];
-    float cg = 0.f, sg = 0.f;  // group correction; group sum of X (asymmetric term)
+    uint32_t X2[64];              // A operand: the lane's group of X if i == gg, else zeros
+    float corr[4] = {0.f, 0.f, 0.f, 0.f};   // the set's group corrections (wave-uniform)
+    float sgv[4] = {0.f, 0.f, 0.f, 0.f};    // the set's group sums of X (asymmetric term)
     int cs = 0, ct = 0;  // step being computed
     auto compute = [&](int j) {
-        const int g = 4 * (w + cs * W) + gg;
-        const bool gvalid = g < G;
+        const int set = w + cs * W;
         if (ct == 0) {
             // New set: stage its X (LDS operations of one wave complete in
             // order, so the previous set's reads are done), read back this
-            // lane's group, and form the group's correction over the quarter.
+            // lane's A operand, and form each group's correction over its
+            // quarter of the wave.
             reinterpret_cast<u32x4_t *>(xw)[lane] = xbuf[j];
+            const uint32_t *src = (i == gg) ? xw + 64 * gg : zblk;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const u32x4_t v = reinterpret_cast<const u32x4_t *>(xw + 64 * gg)[q];
+                const u32x4_t v = reinterpret_cast<const u32x4_t *>(src)[q];
                 X2[4 * q] = v.x; X2[4 * q + 1] = v.y; X2[4 * q + 2] = v.z; X2[4 * q + 3] = v.w;
             }
             const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
             float sx = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) sx = dot2(one, xw[64 * gg + i + 16 * q], sx);
-            cg = row16_sum(my_coef * sx);
+            const float cg = row16_sum(my_coef * sx);
+            float sg = 0.f;
             if constexpr (ASYM) sg = row16_sum(sx);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                corr[v] = lane_value(cg, 16 * v);
+                if constexpr (ASYM) sgv[v] = lane_value(sg, 16 * v);
+            }
         }
-        // four independent dot2 chains (one per 32-column word) keep a wave's
-        // dependent-issue latency off the critical path
-        float P4[4];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             uint32_t Pw[R];
@@ -190,38 +225,55 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
             for (int p = 0; p < R; ++p) Pw[p] = buf[j][p][d];
             uint32_t D0[16], D1[16];
             decode_word<R>(Pw, D0, D1);
-            float Pd = 0.f;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                Pd = dot2(D0[m], X2[16 * d + m], Pd);
-                if constexpr (Phases<R>::count == 2) Pd = dot2(D1[m], X2[16 * d + m], Pd);
+            for (int c = 0; c < 4; ++c) {
+                const u32x4_t a = {X2[16 * d + 4 * c], X2[16 * d + 4 * c + 1], X2[16 * d + 4 * c + 2],
+                                   X2[16 * d + 4 * c + 3]};
+                const u32x4_t b0 = {D0[4 * c], D0[4 * c + 1], D0[4 * c + 2], D0[4 * c + 3]};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                              __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
+                if constexpr (NPH == 2) {
+                    const u32x4_t b1 = {D1[4 * c], D1[4 * c + 1], D1[4 * c + 2], D1[4 * c + 3]};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                  __builtin_bit_cast(bf16x8_t, b1), acc, 0, 0, 0);
+                }
             }
-            P4[d] = Pd;
         }
-        const float P = (P4[0] + P4[1]) + (P4[2] + P4[3]);
+        // lane (i, 0): acc[v] = group 4*set + v of row i (lanes of the other
+        // quarters hold the zero rows of A)
         const int row = 16 * (t_begin + ct) + i;
-        const uint32_t sbits = (g & 1) ? (sbuf[j] & 0xFFFF0000u) : (sbuf[j] << 16);
-        const float s = (gvalid && row < n) ? __uint_as_float(sbits) : 0.f;
-        if constexpr (ASYM) {
-            // asymmetric child = symmetric child + s * (127.5 - z) per weight;
-            // in the units of P (which the epilogue scales by 2^(8-R)):
-            const uint32_t zbits = (g & 1) ? (zbuf[j] & 0xFFFF0000u) : (zbuf[j] << 16);
-            const float zc = (127.5f - __uint_as_float(zbits)) * (1.0f / (float)(1 << (8 - R)));
-            return s * fmaf(zc, sg, P + cg);
+        const bool rvalid = row < n;
+        float out = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint32_t wd = (v >> 1) ? sbuf[j].y : sbuf[j].x;
+            const uint32_t sbits = (v & 1) ? (wd & 0xFFFF0000u) : (wd << 16);
+            const float s = rvalid ? __uint_as_float(sbits) : 0.f;
+            float term = acc[v] + corr[v];
+            if constexpr (ASYM) {
+                // asymmetric child = symmetric child + s * (127.5 - z) per
+                // weight; in the units of acc (scaled by 2^(8-R) at the end):
+                const uint32_t zw = (v >> 1) ? zbuf[j].y : zbuf[j].x;
+                const uint32_t zbits = (v & 1) ? (zw & 0xFFFF0000u) : (zw << 16);
+                const float zc = (127.5f - __uint_as_float(zbits)) * (1.0f / (float)(1 << (8 - R)));
+                term = fmaf(zc, sgv[v], term);
+            }
+            out = fmaf(s, term, out);
         }
-        return s * (P + cg);
+        return out;
     };
-    // Accumulate into this lane's own LDS slot for the tile.  Each slot has a
-    // single writer (this lane), so no atomic is needed and the order of the
-    // additions is fixed: the wave's first set stores, later sets read, add
-    // and store.  (LDS float atomics serialize across the CU: one wave-wide
-    // ds_add_f32 per step cost about a microsecond per launch.)
+    // Accumulate into this row's own LDS slot for the tile.  Each slot has a
+    // single writer (lane i of quarter 0), so no atomic is needed and the
+    // order of the additions is fixed: the wave's first set stores, later
+    // sets read, add and store.
     auto commit = [&](float v) {
-        float *slot = &red[(w * slots + ct) * 64 + lane];
-        if (cs == 0)
-            *slot = v;
-        else
-            *slot += v;
+        if (gg == 0) {
+            float *slot = &red[(w * slots + ct) * 16 + i];
+            if (cs == 0)
+                *slot = v;
+            else
+                *slot += v;
+        }
         if (++ct == T) {
             ct = 0;
             ++cs;
@@ -233,6 +285,14 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
 #pragma unroll
         for (int j = 0; j < PD; ++j) {
             const float v = compute(j);
+            // The refill goes after every use of the buffer's registers: a
+            // load issued while the old value is still to be read would need
+            // a second register, and the copy between the two at the loop's
+            // back edge would wait for every load in flight.  (The empty asm
+            // keeps the step's result -- and its reads of the scales -- here,
+            // instead of sunk into the branch of the lanes that store it.)
+            asm volatile("" : : "v"(v));
+            __builtin_amdgcn_sched_barrier(0);
             load_step(j);  // refill as soon as the buffer is free
             commit(v);
             // Keep the next step's uses of the refilled registers in the next
@@ -244,23 +304,20 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     for (int j = 0; j < PD; ++j)  // the last < PD steps are already loaded
         if (Ufull + j < U) commit(compute(j));
 
-    // Rows: add the four groups of each set and the waves, in a fixed order.
+    // Rows: add the waves, in a fixed order.
     __syncthreads();
     const float post = (float)(1 << (8 - R));
     for (int e = threadIdx.x; e < T * 16; e += blockDim.x) {
         const int t = e >> 4, ii = e & 15;
         float sum = 0.f;
-        for (int ww = 0; ww < W; ++ww) {
-            const float *slot = red + (ww * slots + t) * 64 + ii;
-            sum += (slot[0] + slot[16]) + (slot[32] + slot[48]);
-        }
+        for (int ww = 0; ww < W; ++ww) sum += red[(ww * slots + t) * 16 + ii];
         const int row = 16 * t_begin + e;
         if (row < n) store_y(y, ybf16, row, sum * post);
     }
 }
 
-// Odd group counts (k = 128 * odd) would need 16-bit scale loads, and very
-// large k would not fit X in LDS; these rare shapes take this plain one-tile
+// Group counts that are not multiples of 4 (k = 128 * g, g % 4 != 0) would
+// need narrower scale loads; these rare shapes take this plain one-tile
 // kernel: one workgroup per 16-row tile.
 template <int R>
 __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restrict__ x,
@@ -333,7 +390,7 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
 }
 
 template <int R, int PD, bool ASYM>
-__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_kernel(const uint16_t *__restrict__ x,
                                                                   const uint8_t *__restrict__ planes,
                                                                   int64_t plane_bytes,
                                                                   const uint16_t *__restrict__ scales,
@@ -366,7 +423,7 @@ struct GemvGroup {
 
 // Workgroup b runs item b; items are numbered product by product.  Every
 // item has `slots` partial-sum slots per wave (the largest tpw of the group).
-__global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_group_kernel(GemvGroup grp) {
+__global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_group_kernel(GemvGroup grp) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int item = blockIdx.x;
     int jb = 0;
@@ -394,9 +451,8 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES) void gemv_group_kernel(GemvGro
 
 // ---------------------------------------------------------------- host side
 
-// Launch shape of the streaming kernel.  Eight waves per workgroup (two per
-// SIMD: one wave alone leaves the decode's dependent-issue gaps unfilled) and
-// about one workgroup per CU, each owning a run of 16-row tiles.
+// Launch shape of the streaming kernel.  Eight waves per workgroup and about
+// GEMV_WGS_PER_CU workgroups per CU, each owning a run of 16-row tiles.
 struct GemvPlan {
     int waves, tpw;
     bool deep;  // prefetch depth gemv_depth(r), else GEMV_DEPTH_SHORT
@@ -406,7 +462,8 @@ static GemvPlan gemv_plan(int n, int k, int r, int cu_count) {
     const int tiles = (n + 15) / 16;
     GemvPlan p;
     p.waves = GEMV_MAX_WAVES;
-    int tpw = (tiles + cu_count / 2) / cu_count;  // about one workgroup per CU
+    const int wgs = GEMV_WGS_PER_CU * cu_count;
+    int tpw = (tiles + wgs / 2) / wgs;  // about GEMV_WGS_PER_CU workgroups per CU
     if (tpw > GEMV_MAX_TILES) tpw = GEMV_MAX_TILES;
     if (tpw < 1) tpw = 1;
     p.tpw = tpw;
@@ -480,9 +537,10 @@ void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
 
 int gemv_group_capacity() { return GEMV_MAX_GROUP; }
 
-// The streaming kernel reads scales as aligned 32-bit words: it takes even
-// group counts (every other shape goes to the plain one-tile kernel).
-static bool gemv_streamable(int k) { return ((k / 128) & 1) == 0; }
+// The streaming kernel reads the scales of a set's four groups as one aligned
+// 8-byte word: it takes group counts that are multiples of 4 (every other
+// shape goes to the plain one-tile kernel).
+static bool gemv_streamable(int k) { return ((k / 128) & 3) == 0; }
 
 bool gemv_group_eligible(const QgemmArgs &a) {
     return a.batch == 1 && gemv_streamable(a.k) && !a.zeros && !a.ybf16;

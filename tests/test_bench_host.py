@@ -1,15 +1,16 @@
-"""bench.py on the CPU: its one-GPU contract, and the counter summaries that
-write the committed traffic evidence.
+"""bench.py on the CPU: its one-GPU contract, and the counter and trace
+summaries that write the committed profiling evidence.
 
-Asked for more than one GPU (by flag
-or by a launcher's WORLD_SIZE) it exits with status 2 and says why, before
-touching a GPU."""
+Asked for more than one GPU (by flag or by a launcher's WORLD_SIZE) it exits
+with status 2 and says why, before touching a GPU.  The summaries are fed
+synthetic rocprofv3 CSV files whose true values are known."""
 import os
 import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 BENCH = os.path.join(ROOT, "bench.py")
+sys.path.insert(0, ROOT)
 
 
 def _run(args, env_extra=None):
@@ -30,45 +31,125 @@ def test_more_than_one_rank_by_world_size_exits_2():
     assert "WORLD_SIZE=4" in res.stderr and res.stdout == ""
 
 
-def _write_counters(folder, rows):
-    os.makedirs(os.path.join(folder, "vm"), exist_ok=True)
-    with open(os.path.join(folder, "vm", "1_counter_collection.csv"), "w") as f:
-        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
-        for i, (name, counter, value) in enumerate(rows):
-            f.write(f'{i},"{name}",{counter},{value}\n')
+def test_unknown_section_is_refused():
+    res = _run(["--only", "b1,nonsense"])
+    assert res.returncode != 0 and "nonsense" in res.stderr
 
 
-def test_counter_summaries_scale_by_the_reference_copy(tmp_path, monkeypatch):
-    sys.path.insert(0, ROOT)
+def test_rotation_rule():
     import bench
-    import synth
-    n, k = next((n, k) for nm, n, k in synth.WORKLOADS["llama3.1-8b"] if nm == "gate_up")
-    copy_kib = bench.PROBE_COPY_BYTES / 2 / 1024  # a counter that reports half the bytes
-    # per-width pass: every launch fetches exactly planes + scales + X
-    rows = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib)]
-    for r in bench.RBITS_RS:
-        exact = r * n * k // 8 + n * k // 64 + 2 * k
-        rows += [(f"void nbw::gemv_kernel<{r}, 2, false>(args)", "FETCH_SIZE", exact / 2 / 1024)] * 3
-    _write_counters(str(tmp_path / "rb"), rows)
-    monkeypatch.setattr(bench, "RBITS_FILE", str(tmp_path / "rbits.txt"))
-    bench.rbits_from(str(tmp_path / "rb"))
-    text = open(tmp_path / "rbits.txt").read()
-    assert "factor 2.0000" in text
-    table = [line for line in text.splitlines() if line.startswith("| ") and "`nbw::gemv_kernel<" in line]
-    assert len(table) == len(bench.RBITS_RS)
-    for line in table:
-        assert line.split("|")[6].strip() == "1.0000"  # fetched / (planes + scales + X)
-    # traffic pass: fetched and written bytes of the dominant kernel per launch
-    fetch = [("__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib),
-             ("void nbw::gemv_kernel<4, 2, false>(args)", "FETCH_SIZE", 1000.0),
-             ("void nbw::gemv_kernel<4, 2, false>(args)", "FETCH_SIZE", 3000.0)]
-    write = [("__amd_rocclr_copyBuffer", "WRITE_SIZE", bench.PROBE_COPY_BYTES / 1024),
-             ("void nbw::gemv_kernel<4, 2, false>(args)", "WRITE_SIZE", 64.0),
-             ("void nbw::gemv_kernel<4, 2, false>(args)", "WRITE_SIZE", 64.0)]
-    _write_counters(str(tmp_path / "f"), fetch)
-    _write_counters(str(tmp_path / "w"), write)
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.txt"))
-    bench.traffic_from(str(tmp_path / "f"), str(tmp_path / "w"))
-    kv = dict(line.split(": ", 1) for line in open(tmp_path / "traffic.txt").read().splitlines() if ": " in line)
-    assert float(kv["traffic_bytes_per_launch"]) == 2 * 2000.0 * 1024 + 64.0 * 1024
-    assert kv["kernel_source_sha256_16"].strip() == bench.kernel_source_hash()
+    # >= 600 MB of other bytes between two uses: ceil(600 MB / bytes) + 1 copies
+    assert bench.rule_copies(600_000_000) == 2
+    assert bench.rule_copies(599_999_999) == 3
+    assert bench.rule_copies(4_194_304) == 145
+    for nb in (1_000_000, 54_525_952, 176_160_768):
+        c = bench.rule_copies(nb)
+        assert (c - 1) * nb >= bench.ROTATE_BYTES > (c - 2) * nb
+
+
+def _write_counters(path, rows):
+    """rows: (dispatch id, kernel, counter, value, start ns, end ns)"""
+    os.makedirs(os.path.join(path, "host"), exist_ok=True)
+    with open(os.path.join(path, "host", "7_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
+        for d, name, c, v, t0, t1 in rows:
+            f.write(f'{d},"{name}",{c},{v},{t0},{t1}\n')
+
+
+def test_counter_summary_maps_launches_and_scales_bytes(tmp_path, monkeypatch):
+    import bench_counters as bc
+    monkeypatch.setattr(bc, "PROFILES", str(tmp_path))
+    kind = "gemm_b256"
+    prods = bc.PROBES[kind][2]
+    copy_kib = bc.PROBE_COPY_BYTES / 2 / 1024   # a counter that reports half the bytes
+    fetch, sq = [], []
+    d = 0
+    # set-up dispatches before the reference copy: a clone (a smaller copy) and a warm launch
+    for rows in (fetch, sq):
+        rows.append((0, "__amd_rocclr_copyBuffer", "FETCH_SIZE" if rows is fetch else "GRBM_GUI_ACTIVE",
+                     10.0, 0, 1000))
+        rows.append((1, "void nbw::gemm_wide_kernel<8, 4>(args)", "FETCH_SIZE" if rows is fetch else "GRBM_GUI_ACTIVE",
+                     99.0, 0, 1000))
+    fetch.append((2, "__amd_rocclr_copyBuffer", "FETCH_SIZE", copy_kib, 0, 1000))
+    sq.append((2, "__amd_rocclr_copyBuffer", "GRBM_GUI_ACTIVE", 8.0, 0, 1000))
+    d = 3
+    truth = {}
+    for j, (wl, lin, b, r) in enumerate(prods):
+        alg = bc.algorithmic((wl, lin, b, r))["bytes"]
+        split = lin in ("o", "down")
+        truth[j] = (alg, split)
+        for _ in range(bc.PROBE_LAUNCHES):
+            name = f"void nbw::gemm_wide_kernel<{r}, 4>(args)"
+            fetch.append((d, name, "FETCH_SIZE", alg / 2 / 1024, 0, 20_000))
+            sq.append((d, name, "SQ_BUSY_CYCLES", 32 * 44_000.0, 0, 20_000))   # 44000 cycles in 20 us: 2.2 GHz
+            sq.append((d, name, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 11_000.0, 0, 20_000))
+            sq.append((d, name, "SQ_INSTS_MFMA", 1000.0, 0, 20_000))
+            sq.append((d, name, "SQ_INSTS_VALU", 5000.0, 0, 20_000))
+            d += 1
+            if split:
+                red = "void nbw::gemm_wide_reduce_kernel<4>(args)"
+                fetch.append((d, red, "FETCH_SIZE", 512.0, 0, 2000))
+                sq.append((d, red, "GRBM_GUI_ACTIVE", 800.0, 0, 2000))
+                d += 1
+    _write_counters(str(tmp_path / "fetch"), fetch)
+    _write_counters(str(tmp_path / "sq"), sq)
+    summ = bc.pmc_summary(kind, [str(tmp_path / "fetch"), str(tmp_path / "sq")])
+    text = open(tmp_path / f"counters_{kind}.md").read()
+    assert "FETCH_SIZE factor: 2.0000" in text
+    assert f"kernel_source_sha256_16: {bc.source_hash(bc.PROBES[kind][1])}" in text
+    for j, prod in enumerate(prods):
+        row = summ[prod]
+        alg, split = truth[j]
+        extra = 512.0 * 1024 * 2 if split else 0.0
+        assert abs(row["hbm_bytes"] - (alg + extra)) < 1e-6 * alg
+        assert abs(row["mfma_busy"] - 0.25) < 1e-12
+        assert abs(row["clock_ghz"] - 2.2) < 1e-12
+        assert abs(row["valu_per_mfma"] - 4.0) < 1e-12
+        assert abs(row["valu_busy"] - 4 * 4000 / (1024 * 44_000)) < 1e-12
+        assert row["kernel"].startswith("nbw::gemm_wide_kernel<")
+    # the roofline's traffic: the file read back while the sources are unchanged
+    t = bc.stored_traffic(kind, [prods[0], prods[2]])
+    assert abs(t - (truth[0][0] + truth[2][0]) / 2) < 1.0
+    # a stale stamp gives no traffic
+    path = tmp_path / f"counters_{kind}.md"
+    path.write_text(path.read_text().replace("kernel_source_sha256_16: ", "kernel_source_sha256_16: x"))
+    assert bc.stored_traffic(kind, [prods[0]]) is None
+
+
+def test_counter_summary_refuses_a_wrong_launch_count(tmp_path, monkeypatch):
+    import pytest
+    import bench_counters as bc
+    monkeypatch.setattr(bc, "PROFILES", str(tmp_path))
+    rows = [(0, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 1.0, 0, 1),
+            (1, "void nbw::pack_kernel(args)", "FETCH_SIZE", 1.0, 0, 1)]
+    _write_counters(str(tmp_path / "p"), rows)
+    with pytest.raises(SystemExit):
+        bc.pmc_summary("pack", [str(tmp_path / "p")])
+
+
+def test_trace_summary_attributes_the_split_add(tmp_path, monkeypatch):
+    import bench_counters as bc
+    monkeypatch.setattr(bc, "PROFILES", str(tmp_path))
+    os.makedirs(tmp_path / "t" / "host")
+    rows = []
+    t = 0
+    for _ in range(4):   # unsplit 100 us launches, then split 20 us launches + 4 us adds
+        rows.append(("void nbw::gemm_wide_kernel<8, 4>(a)", t, t + 100_000, "57344"))
+        t += 101_000
+        rows.append(("void nbw::gemm_wide_kernel<8, 4>(a)", t, t + 20_000, "8192"))
+        t += 21_000
+        rows.append(("void nbw::gemm_wide_reduce_kernel<4>(a)", t, t + 4_000, "4096"))
+        t += 5_000
+        rows.append(("__amd_rocclr_fillBufferAligned", t, t + 1_000, "64"))
+        t += 2_000
+    with open(tmp_path / "t" / "host" / "7_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp,Grid_Size_X,Grid_Size_Y,Grid_Size_Z\n")
+        for name, a, b, gx in rows:
+            f.write(f'"{name}",{a},{b},{gx},2,1\n')
+    out = bc.trace_summary("b256", str(tmp_path / "t"), "cmd")
+    g = out["nbw::gemm_wide_kernel<8, 4>"]
+    assert g["calls"] == 8
+    assert abs(g["avg_us"] - 60.0) < 1e-9
+    assert abs(g["launch_us"] - 62.0) < 1e-9     # (4 x 100 + 4 x (20 + 4)) / 8
+    text = open(tmp_path / "trace_b256.md").read()
+    assert "| `nbw::gemm_wide_kernel<8, 4>` 8192x2x1 | 4 | 20.00 | 4 | 4.00 | 24.00 |" in text
