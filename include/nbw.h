@@ -250,9 +250,11 @@ typedef struct nbw_problem {
  * precision execution over heterogeneous per-layer bit-widths).  Results are
  * those of calling nbw_qgemm on each problem in order on `stream`; since the
  * problems may run concurrently, no problem's output may overlap another's
- * inputs or output.  Batch-1 problems run as one grouped launch (up to 32
- * per launch); others are queued one by one.  Every problem is validated
- * before anything is queued. */
+ * inputs or output.  Batch-1 problems run as one grouped launch of the
+ * streaming kernel and batch-2..16 problems (k/128 a multiple of 4) as one
+ * grouped launch of the small-batch kernel (up to 32 products per launch),
+ * each bit-identical to its single call; others are queued one by one.
+ * Every problem is validated before anything is queued. */
 nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *stream);
 
 /* Child codes q_r = c >> (8 - r) read back from planes 0..r-1 of `w`, through

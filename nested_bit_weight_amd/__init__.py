@@ -415,7 +415,9 @@ def qgemm_grouped(items, outs=None):
     """Several products in as few dispatches as possible.
 
     ``items``: sequence of ``(x, w, scales, r)`` as for :func:`qgemm`.  Returns the
-    fp32 outputs (or fills ``outs``).  Batch-1 products run as one grouped launch."""
+    fp32 outputs (or fills ``outs``).  Batch-1 products run as one grouped launch of
+    the streaming kernel, batch-2..16 products (k/128 a multiple of 4) as one of the
+    small-batch kernel; the rest one by one."""
     items = list(items)
     if outs is None:
         outs = [None] * len(items)

@@ -280,15 +280,25 @@ nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *s
     int cus = 0;
     nbw_status st = cu_count(&cus);
     if (st != NBW_OK) return st;
-    std::vector<nbw::QgemmArgs> group;
-    std::vector<int> rs;
-    const int cap = nbw::gemv_group_capacity();
+    // Batch-1 products go to the streaming kernel's grouped launch, batch
+    // 2..16 ones to the small-batch kernel's; each flushes when full.
+    std::vector<nbw::QgemmArgs> group, sgroup;
+    std::vector<int> rs, srs;
+    const int cap = nbw::gemv_group_capacity(), scap = nbw::smallb_group_capacity();
     auto flush = [&]() -> nbw_status {
         if (group.empty()) return NBW_OK;
         hipError_t e = nbw::launch_gemv_group(group.data(), rs.data(), (int)group.size(), cus,
                                               (hipStream_t)stream);
         group.clear();
         rs.clear();
+        return e == hipSuccess ? NBW_OK : hip_failed(e);
+    };
+    auto sflush = [&]() -> nbw_status {
+        if (sgroup.empty()) return NBW_OK;
+        hipError_t e = nbw::launch_smallb_group(sgroup.data(), srs.data(), (int)sgroup.size(), cus,
+                                                (hipStream_t)stream);
+        sgroup.clear();
+        srs.clear();
         return e == hipSuccess ? NBW_OK : hip_failed(e);
     };
     for (int32_t j = 0; j < count; ++j) {
@@ -307,12 +317,17 @@ nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *s
             group.push_back(a);
             rs.push_back(pr.r);
             if ((int)group.size() == cap && (st = flush()) != NBW_OK) return st;
+        } else if (nbw::smallb_group_eligible(a)) {
+            sgroup.push_back(a);
+            srs.push_back(pr.r);
+            if ((int)sgroup.size() == scap && (st = sflush()) != NBW_OK) return st;
         } else {
             st = nbw_qgemm(pr.x_bf16, pr.batch, &pr.w, pr.scales_bf16, pr.r, pr.y, stream);
             if (st != NBW_OK) return st;
         }
     }
-    return flush();
+    if ((st = flush()) != NBW_OK) return st;
+    return sflush();
 }
 
 nbw_status nbw_qgemm(const void *x_bf16, int64_t batch, const nbw_wview *w,

@@ -74,6 +74,13 @@ bool gemv_group_eligible(const QgemmArgs &a);
 hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
                              hipStream_t stream);
 
+// Grouped small-batch launch: several batch-2..16 products (each with its own
+// r) as one dispatch, bit-identical to their single launches.
+int smallb_group_capacity();
+bool smallb_group_eligible(const QgemmArgs &a);
+hipError_t launch_smallb_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
+                               hipStream_t stream);
+
 // Name of the kernel template instance the launcher above would use (as
 // rocprofv3 prints it, without the parameter list).
 void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len);

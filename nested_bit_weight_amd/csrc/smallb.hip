@@ -103,13 +103,15 @@ constexpr int SMALLB_NB2_MAX_TILES = 7;
 // NB: 16-row batch slices per workgroup.  Each decoded weight fragment feeds
 // the MFMAs of every slice, so the plane decode, the dominant cost, is paid
 // once per NB slices.
+// One workgroup's work: tile run bx (tiles bx*tiles_per_wg ...) and batch
+// pass by of one product.  red: the dynamic LDS, [W][tiles_per_wg][NB][4][64]
+// partial sums, then [W] activation buffers.
 template <int R, int PD, bool ASYM, bool S4, int NB>
-__global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
+__device__ __forceinline__ void smallb_tiles(
     const uint16_t *__restrict__ x, int64_t batch, int64_t ldx, const uint8_t *__restrict__ planes,
     int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     int n, int k, int tiles_total, int tiles_per_wg, float *__restrict__ y, int64_t ldy,
-    int ybf16) {
-    extern __shared__ __align__(16) float red[];  // [W][tiles_per_wg][NB][4][64], then [W] x buffers
+    int ybf16, int bx, int by, float *red) {
     constexpr int NPH = Phases<R>::count;
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
@@ -117,9 +119,9 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, d = lane >> 4;
-    const int t_begin = blockIdx.x * tiles_per_wg;
+    const int t_begin = bx * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    const int64_t b0 = (int64_t)blockIdx.y * 16 * NB;
+    const int64_t b0 = (int64_t)by * 16 * NB;
 
     // This wave's sets: ordinal s = 0 .. my_sets-1 is set w + s*W.
     const int my_sets = nsets > w ? (nsets - w + W - 1) / W : 0;
@@ -413,6 +415,68 @@ __global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
     }
 }
 
+template <int R, int PD, bool ASYM, bool S4, int NB>
+__global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_kernel(
+    const uint16_t *__restrict__ x, int64_t batch, int64_t ldx, const uint8_t *__restrict__ planes,
+    int64_t plane_bytes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    int n, int k, int tiles_total, int tiles_per_wg, float *__restrict__ y, int64_t ldy,
+    int ybf16) {
+    extern __shared__ __align__(16) float red[];
+    smallb_tiles<R, PD, ASYM, S4, NB>(x, batch, ldx, planes, plane_bytes, scales, zeros, n, k, tiles_total,
+                                      tiles_per_wg, y, ldy, ybf16, blockIdx.x, blockIdx.y, red);
+}
+
+// ---------------------------------------------------------------- grouped launch
+
+// Several batch-2..16 products, each with its own r (MatGPTQ: Accurate and
+// Efficient Post-Training Matryoshka Quantization, abstract: mixed-precision
+// execution over heterogeneous per-layer bit-widths), as one dispatch.
+// Workgroup b runs item b; items are numbered product by product, each product
+// with its own tile run length.  Eligible: symmetric children, k/128 a
+// multiple of 4, dense X and fp32 Y -- the single launch's smallb_kernel<R,
+// SMALLB_DEPTH, false, true, 1>, so a grouped product is bit-identical to it.
+constexpr int SMALLB_MAX_GROUP = 32;
+
+struct SmallbJob {
+    const uint16_t *x;
+    const uint8_t *planes;
+    int64_t plane_bytes;
+    const uint16_t *scales;
+    float *y;
+    int batch, n, k, r, tiles, tpw, item_begin;
+};
+
+struct SmallbGroup {
+    SmallbJob job[SMALLB_MAX_GROUP];
+    int count;
+};
+
+__global__ __launch_bounds__(64 * SMALLB_WAVES) void smallb_group_kernel(SmallbGroup grp) {
+    extern __shared__ __align__(16) float red[];
+    const int item = blockIdx.x;
+    int jb = 0;
+    while (jb + 1 < grp.count && item >= grp.job[jb + 1].item_begin) ++jb;
+    const SmallbJob &J = grp.job[jb];
+    const int bx = item - J.item_begin;
+    switch (J.r) {
+#define NBW_SMALLB_CASE(RR)                                                                          \
+    case RR:                                                                                         \
+        smallb_tiles<RR, SMALLB_DEPTH, false, true, 1>(J.x, J.batch, J.k, J.planes, J.plane_bytes,   \
+                                                       J.scales, nullptr, J.n, J.k, J.tiles, J.tpw, \
+                                                       J.y, J.n, 0, bx, 0, red);                     \
+        break;
+        NBW_SMALLB_CASE(1)
+        NBW_SMALLB_CASE(2)
+        NBW_SMALLB_CASE(3)
+        NBW_SMALLB_CASE(4)
+        NBW_SMALLB_CASE(5)
+        NBW_SMALLB_CASE(6)
+        NBW_SMALLB_CASE(7)
+        NBW_SMALLB_CASE(8)
+#undef NBW_SMALLB_CASE
+    }
+}
+
 // About one workgroup per CU, each owning a run of 16-row tiles.
 static int smallb_tpw(const QgemmArgs &a, int cu_count) {
     const int tiles = (a.n + 15) / 16;
@@ -472,6 +536,41 @@ static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
 void smallb_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
     snprintf(out, len, "nbw::smallb_kernel<%d, %d, %s, %s, %d>", r, SMALLB_DEPTH, a.zeros ? "true" : "false",
              ((a.k / 128) & 3) == 0 ? "true" : "false", smallb_nb(r, a, cu_count));
+}
+
+int smallb_group_capacity() { return SMALLB_MAX_GROUP; }
+
+bool smallb_group_eligible(const QgemmArgs &a) {
+    return a.batch >= 2 && a.batch <= 16 && ((a.k / 128) & 3) == 0 && !a.zeros && !a.ybf16 &&
+           (a.ldx == 0 || a.ldx == a.k) && (a.ldy == 0 || a.ldy == a.n);
+}
+
+hipError_t launch_smallb_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
+                               hipStream_t stream) {
+    SmallbGroup grp = {};
+    grp.count = count;
+    int items = 0, slots = 1;
+    for (int j = 0; j < count; ++j) {
+        const QgemmArgs &a = probs[j];
+        SmallbJob &J = grp.job[j];
+        J.x = a.x;
+        J.planes = a.planes;
+        J.plane_bytes = a.plane_bytes;
+        J.scales = a.scales;
+        J.y = a.y;
+        J.batch = (int)a.batch;
+        J.n = a.n;
+        J.k = a.k;
+        J.r = rs[j];
+        J.tiles = (a.n + 15) / 16;
+        J.tpw = smallb_tpw(a, cu_count);
+        if (J.tpw > slots) slots = J.tpw;
+        J.item_begin = items;
+        items += (J.tiles + J.tpw - 1) / J.tpw;
+    }
+    hipLaunchKernelGGL(smallb_group_kernel, dim3(items), dim3(64 * SMALLB_WAVES),
+                       smallb_lds_bytes(SMALLB_WAVES, slots, 1), stream, grp);
+    return hipGetLastError();
 }
 
 hipError_t launch_smallb(int r, const QgemmArgs &a, int cu_count, hipStream_t stream) {

@@ -333,3 +333,47 @@ def test_grouped_llama8b_layer_sampled(nbw):
         n = d["n"]
         rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(n).integers(0, n, 40)]))
         assert rel_err(y.cpu().numpy()[:, rows], oracle_rows(d, r, rows)) <= DESIGN_BOUND
+
+
+def test_grouped_small_batches_match_single_launches_and_oracle(nbw):
+    # Batch 2..16 products with mixed widths (1..8) and ragged n in one grouped
+    # dispatch of the small-batch kernel: bit-identical to its single launch
+    # (the same per-output summation order), within the design bound of the oracle.
+    specs = [(1000, 1024, 16, 4), (48, 512, 2, 2), (333, 2048, 9, 3), (64, 512, 16, 8),
+             (200, 1024, 5, 6), (17, 512, 3, 1), (130, 1536, 12, 5), (96, 512, 7, 7)]
+    items, host = _grouped_case(nbw, specs, seed=90)
+    outs = nbw.qgemm_grouped(items)
+    torch.cuda.synchronize()
+    for (x, w, s, r), y, (case, _) in zip(items, outs, host):
+        single = nbw.qgemm(x, w, s, r, kernel="smallb")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), single.cpu().numpy())
+        ref = oracle.qgemm(case["x"], oracle.pack(case["codes"]), case["scales"], case["n"],
+                           case["k"], r)
+        assert rel_err(y.cpu().numpy(), ref) <= DESIGN_BOUND
+
+
+def test_grouped_llama8b_layer_batch16_mixed_widths_sampled(nbw):
+    # The four Llama-3.1-8B linears at full size and batch 16 (the bench's
+    # activations), each with its own width, as one grouped dispatch.
+    widths = (4, 3, 2, 6)
+    wid = synth.WORKLOAD_IDS["llama3.1-8b"]
+    items, ds, xs = [], [], []
+    for sid, r in enumerate(widths):
+        d = synth.make_linear("llama3.1-8b", sid, 1)
+        xb = synth.activations(16, d["k"], synth.rng_for(0, wid, sid, synth.T_X))
+        w = nbw.pack_bitplanes(dev(d["codes"]))
+        items.append((dev(xb, torch.bfloat16), nbw.slice_view(w, r), dev(d["scales"], torch.bfloat16), r))
+        ds.append(d)
+        xs.append(xb)
+    outs = nbw.qgemm_grouped(items)
+    torch.cuda.synchronize()
+    for (x, w, s, r), y, d, xb in zip(items, outs, ds, xs):
+        n = d["n"]
+        rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
+                                         np.random.default_rng(n).integers(0, n, 40)]))
+        planes = oracle.pack(np.ascontiguousarray(d["codes"][rows]))
+        ref = oracle.qgemm(xb, planes, np.ascontiguousarray(d["scales"][rows]), len(rows), d["k"], r)
+        e = rel_err(y.cpu().numpy()[:, rows], ref)
+        print(f"grouped b16 {d['name']} r={r} err={e:.3e}", flush=True)
+        assert e <= CONTRACT and e <= DESIGN_BOUND
