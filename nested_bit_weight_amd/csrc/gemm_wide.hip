@@ -1,4 +1,4 @@
-// gemm_wide.hip -- large-batch dequant-GEMM, one wave per SIMD, gfx950.
+// gemm_wide.hip -- large-batch dequant-GEMM for symmetric children, gfx950.
 //
 // Y[b][i] = sum_j X[b][j] * s[i][j/128] * 2^(8-r) * (q_r[i][j] + 1/2 - 2^(r-1)),
 // the r-bit child of a sliceable parent (MatGPTQ: Efficient and Accurate
@@ -6,38 +6,43 @@
 // sizes beyond one; Figure 1: kernel speed-up swept over batch sizes).  At
 // batch 128-256 the product is a dense contraction bound by the MFMA rate, and
 // decoding the bit-planes is the VALU work that has to hide under it.  This
-// kernel decodes every weight exactly once per product and keeps the VALU work
-// per matrix instruction small:
+// kernel decodes every weight once per workgroup and keeps the VALU work per
+// matrix instruction small:
 //
-//  - a workgroup owns 128 weight rows x BM = 32*NBT batch rows (NBT = 4 or 8:
-//    the whole batch of 256 in one tile) and a range of 128-wide groups; each
-//    of its 4 waves (one per SIMD) owns 32 weight rows and ALL BM batch rows,
-//    so a weight row is decoded by one wave of one workgroup only.  D = A.B
-//    with v_mfma_f32_32x32x16_bf16, A = X (rows: batch), B = decoded weights
+//  - a workgroup owns 256 weight rows x BM = 32*NBT batch rows (NBT = 4: 128
+//    batch rows) and a range of 128-wide groups; each of its 8 waves (two per
+//    SIMD) owns 32 weight rows and ALL BM batch rows, so a weight row is
+//    decoded by one wave per BM batch rows.  D = A.B with
+//    v_mfma_f32_32x32x16_bf16, A = X (rows: batch), B = decoded weights
 //    (columns: weight rows).
-//  - B operands are decoded in registers one group ahead (decode.h; lane
-//    (weight row l%32, half h) decodes columns 64h..64h+63 of its row's group,
-//    k-step j takes its pairs 4j..4j+3, i.e. columns 64h+8j..64h+8j+7).
+//  - B operands are decoded in registers at the start of each group
+//    (decode.h; lane (weight row l%32, half h) decodes columns 64h..64h+63 of
+//    its row's group, k-step j takes its pairs 4j..4j+3, i.e. columns
+//    64h+8j..64h+8j+7), while the next group's planes are in flight.
 //  - A operands come from LDS.  X reaches LDS by direct global->LDS loads
-//    (global_load_lds_dwordx4, no registers), double buffered per group.  One
-//    load instruction fills a 1 KB block holding four batch rows 16 apart; a
-//    16-byte pad after each block puts the 16 rows a quarter-wave reads at 16
-//    different bank groups, and every fragment address is a per-lane base plus
-//    a constant.
+//    (global_load_lds_dwordx4, no registers), double buffered per group and
+//    spread over the chain steps.  One load instruction fills a 1 KB block
+//    holding four batch rows 16 apart; a 16-byte pad after each block puts the
+//    16 rows a quarter-wave reads at 16 different bank groups, and every
+//    fragment address is a per-lane base plus a constant.
 //  - each group's 8-MFMA chain per 32-row batch tile starts from zero and the
-//    group scale (one per lane: the lane's weight row) is folded in fp32 right
-//    after it, so every operand of the chain is exact in bf16.
+//    group scale (one per lane: the lane's weight row) is folded in fp32
+//    after it (software-pipelined: the previous tile's fold runs two FMAs per
+//    MFMA of the next chain), so every operand of the chain is exact in bf16.
 //  - the decode's constant offsets leave, per batch row and group, a
 //    correction sum_k x_k * (1/2 - 2^(r-1) - offset_k) (X only) times the
 //    group scale.  Each wave forms the corrections of NBT/4 batch tiles from the
 //    X fragments it reads anyway, splits each fp32 value exactly into three
 //    bf16 parts, and parks them in LDS; every 8 groups the block of
 //    corrections enters the accumulators as a small bf16 product (corrections
-//    [batch row][part, group] times scales [part, group][weight row]): two
-//    MFMAs per batch tile per 8 groups, exact products, fp32 sums.
+//    [batch row][part, group] times scales [part, group][weight row], the
+//    scales from per-lane LDS slots): two MFMAs per batch tile per 8 groups,
+//    exact products, fp32 sums.
 //  - the waves rotate the order of their batch tiles so that the tiles whose
 //    corrections they form come first; one barrier per group hands over the X
 //    buffers and the corrections.
+//  - where the output tiles leave CUs idle, k splits over workgroups into a
+//    caller workspace and a second launch adds the splits in order.
 #include <cstdio>
 
 #include "decode.h"
