@@ -104,11 +104,19 @@ template <int RP> __host__ __device__ constexpr Pick pick(int m) {
         int t = m & 1, j = m >> 1;
         int sh = j < 3 ? 0 : (j < 6 ? 6 : 12);
         return Pick{t, sh, 2 * j - sh};
+    } else if (RP == 3) {
+        // nibble j holds (code << 1): code bits 4j+1 .. 4j+3.  Nibbles 1 and 2
+        // share one shift (by 5: bits 0..2 and 4..6), so a word takes two
+        // shifts instead of three.
+        int s = m & 3, j = m >> 2;
+        int sh = j == 0 ? 0 : j == 3 ? 9 : 5;
+        int lsb = j == 0 ? 1 : j == 1 ? 0 : 4;
+        return Pick{s, sh, lsb};
     } else {
         int s = m & 3, j = m >> 2;
         int sh = j == 0 ? 0 : 4 * j - 3;
         int nib = j == 0 ? 0 : 3;      // nibble's bit 0 after the shift
-        return Pick{s, sh, nib + (RP == 3 ? 1 : 0)};
+        return Pick{s, sh, nib};
     }
 }
 
