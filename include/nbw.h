@@ -86,13 +86,13 @@ typedef struct nbw_wview {
 } nbw_wview;
 
 /* Kernel selectors for nbw_qgemm_kernel.  NBW_KERNEL_AUTO picks by batch:
- * 1 -> GEMV; otherwise SMALLB while it needs one pass over the planes, or
+ * 1..4 -> GEMV; otherwise SMALLB while it needs one pass over the planes, or
  * two passes and k <= 8192 (a pass covers 32 batch rows for r <= 4 when the
- * workgroups' tile runs are short, else 16); otherwise GEMM.  Batches 2..16
+ * workgroups' tile runs are short, else 16); otherwise GEMM.  Batches 5..16
  * always take SMALLB and batches above 64 always GEMM. */
 typedef enum nbw_kernel {
     NBW_KERNEL_AUTO = 0,
-    NBW_KERNEL_GEMV = 1,   /* VALU dequant + bf16 dot2, batch 1..2 per launch slice */
+    NBW_KERNEL_GEMV = 1,   /* streaming dequant feeding MFMA, 4 batch rows per launch */
     NBW_KERNEL_SMALLB = 2, /* in-register dequant feeding MFMA, 16 or 32 batch rows per pass */
     NBW_KERNEL_GEMM = 3    /* large-batch MFMA kernel */
 } nbw_kernel;
@@ -250,10 +250,11 @@ typedef struct nbw_problem {
  * precision execution over heterogeneous per-layer bit-widths).  Results are
  * those of calling nbw_qgemm on each problem in order on `stream`; since the
  * problems may run concurrently, no problem's output may overlap another's
- * inputs or output.  Batch-1 problems run as one grouped launch of the
- * streaming kernel and batch-2..16 problems (k/128 a multiple of 4) as one
- * grouped launch of the small-batch kernel (up to 32 products per launch),
- * each bit-identical to its single call; others are queued one by one.
+ * inputs or output.  Batch 1..4 problems run as grouped launches of the
+ * streaming kernel (one for batch 1, one for batch 2..4) and batch-5..16
+ * problems as one grouped launch of the small-batch kernel (k/128 a multiple
+ * of 4; up to 32 products per launch), each bit-identical to its single call;
+ * others are queued one by one.
  * Every problem is validated before anything is queued. */
 nbw_status nbw_qgemm_grouped(const nbw_problem *problems, int32_t count, void *stream);
 

@@ -29,6 +29,7 @@
 //    diagonal activation operand that keeps the set's four groups in four
 //    output rows (see gemv_tiles); the group scales are folded in fp32 once
 //    per (row, group), and the waves meet in LDS in a fixed order.
+#include <algorithm>
 #include <cstdio>
 
 #include "decode.h"
@@ -57,19 +58,29 @@ constexpr int GEMV_WGS_PER_CU = 1;
 constexpr int GEMV_DEPTH_SHORT = 1;
 __host__ __device__ constexpr int gemv_depth(int r) { return r <= 6 ? 2 : 1; }
 
-// Dynamic LDS: per wave, one set of X (4 groups x 128 bf16 = 1 KB) and 256
-// bytes of zeros, then the per-row partial sums fp32 [W][slots][16], one slot
-// per tile.
-constexpr int GEMV_WAVE_LDS = 1024 + 256;
-__host__ __device__ constexpr size_t gemv_lds_bytes(int waves, int slots) {
-    return (size_t)waves * GEMV_WAVE_LDS + (size_t)waves * slots * 16 * 4;
+// Batch rows one launch of the streaming kernel takes: 1, or up to 4 (the
+// batch rows fill the rows of the MFMA's activation operand that batch 1
+// leaves at zero; see gemv_tiles).
+constexpr int GEMV_MAX_BATCH = 4;
+
+// Dynamic LDS: per wave, one set of X for each of the NBR batch rows (4
+// groups x 128 bf16 = 1 KB a row) and 256 bytes of zeros, then the partial
+// sums fp32 [W][slots][16 NBR], one slot per tile.
+__host__ __device__ constexpr int gemv_wave_lds(int nbr) { return nbr * 1024 + 256; }
+__host__ __device__ constexpr size_t gemv_lds_bytes(int waves, int slots, int nbr) {
+    return (size_t)waves * gemv_wave_lds(nbr) + (size_t)waves * slots * 16 * nbr * 4;
 }
 
 // Sum over each 16-lane row of the wave, in every lane of the row: DPP quad
 // permutes [1,0,3,2] and [2,3,0,1], then row_half_mirror (lane i of each
 // half-row reads lane 7-i: the other quad) and row_mirror (lane i reads
-// lane 15-i: the other half).  VALU only, no LDS round trip.
+// lane 15-i: the other half).  VALU only, no LDS round trip.  Each add sums
+// two equal partial sums in swapped order, so every lane of the row ends
+// with the same bits -- provided no add is fused with a product that made
+// its input (the fused lane would keep the unrounded product while its
+// partner adds the rounded one), hence no contraction here.
 __device__ __forceinline__ float row16_sum(float v) {
+#pragma clang fp contract(off)
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
@@ -94,36 +105,42 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // v_mfma_f32_16x16x32_bf16 takes 32 columns: lane (i, h) of the wave (i =
 // lane % 16, h = lane / 16) supplies 8 decoded weights of row i, group
 // 4*set + h (B operand) and, as row i of the A operand, the same 8 columns
-// of X if i == h and zeros otherwise.  A is block diagonal, so output row v
-// holds group 4*set + v alone: after the 16 MFMAs of a step (4 words x 4
-// pair quads), lane i holds row i's four group sums in its four accumulator
-// registers, and scales them there.  The 15 zero rows of A are the price of
-// batch 1; the matrix cores are otherwise idle, and the VALU keeps only the
-// decode.
+// of batch row i / 4's X if i % 4 == h and zeros otherwise.  Row 4b + v of A
+// thus holds only batch row b's group 4*set + v, and so does output row
+// 4b + v: after the 16 MFMAs of a step (4 words x 4 pair quads), lane
+// (i, b) holds weight row i's four group sums for batch row b in its four
+// accumulator registers, and scales them there.  At batch 1 (NBR = 1) rows
+// 4..15 of A are zero: the matrix cores are otherwise idle, and up to four
+// batch rows cost the same MFMAs and the same decode as one.  Each batch
+// row's sums are formed exactly as at batch 1 (one row of A, the same
+// summation order), so the results do not depend on NBR.
 //
 // Waves are independent until the final reduction: a wave loads the X of its
 // current set itself (one 16-byte load per lane, part of the step's load
 // stream), stages it in its own 1 KB of LDS and reads back its lanes' A
 // operands, so no barrier -- and no wait for every load in flight -- stands
 // between a wave's first loads and its first step.
-template <int R, int PD, bool ASYM>
-__device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
+template <int R, int PD, bool ASYM, int NBR>
+__device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64_t ldx, int batch,
                                            const uint8_t *__restrict__ planes,
                                            int64_t plane_bytes,
                                            const uint16_t *__restrict__ scales,
                                            const uint16_t *__restrict__ zeros, int n, int k,
                                            int t_begin, int T, int slots, float *__restrict__ y,
-                                           int ybf16, unsigned char *lds) {
+                                           int64_t ldy, int ybf16, unsigned char *lds) {
+    static_assert(NBR == 1 || NBR == GEMV_MAX_BATCH, "one batch row, or up to four");
     constexpr int NPH = Phases<R>::count;
+    constexpr int RW = 16 * NBR;  // partial sums per slot
     const int G = k >> 7;
     const int nsets = (G + 3) >> 2;
     const int W = blockDim.x >> 6;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int i = lane & 15, gg = lane >> 4;
-    uint32_t *xw = reinterpret_cast<uint32_t *>(lds + (size_t)w * GEMV_WAVE_LDS);  // this wave's set of X
-    uint32_t *zblk = xw + 256;                                                      // 256 B of zeros
-    float *red = reinterpret_cast<float *>(lds + (size_t)W * GEMV_WAVE_LDS);        // [W][slots][16]
+    // this wave's set of X, batch row b at xw + 256 b; then 256 B of zeros
+    uint32_t *xw = reinterpret_cast<uint32_t *>(lds + (size_t)w * gemv_wave_lds(NBR));
+    uint32_t *zblk = xw + 256 * NBR;
+    float *red = reinterpret_cast<float *>(lds + (size_t)W * gemv_wave_lds(NBR));  // [W][slots][RW]
 
     // This wave's (set, tile) steps: set ordinal s = 0 .. my_sets-1 is set
     // w + s*W, tile t = 0 .. T-1; step u = s*T + t.
@@ -133,8 +150,8 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     // Zero this wave's partial sums (only this wave writes them until the
     // final barrier) and its zero block.
     zblk[lane] = 0u;
-    if (gg == 0)
-        for (int t = 0; t < T; ++t) red[(w * slots + t) * 16 + i] = 0.f;
+    if (NBR > 1 || gg == 0)
+        for (int t = 0; t < T; ++t) red[(w * slots + t) * RW + (NBR > 1 ? lane : i)] = 0.f;
 
     // Coefficient of this lane's pair sums in the group correction
     // sum_k x_k * (1/2 - 2^(R-1) - offset_k): lane (i, gg) takes the pairs
@@ -146,12 +163,13 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
 
     // Step loads: R plane chunks (row i, group 4*set + gg), the two aligned
     // 32-bit words of the scales of row i's four groups of the set, and the
-    // lane's 16 bytes of the set's X (the same chunk for every tile of a set;
-    // reloading it keeps the number of loads per step fixed).  All loads are
+    // lane's 16 bytes of the set's X of each batch row (the same chunks for
+    // every tile of a set; reloading them keeps the number of loads per step
+    // fixed; batch rows past the last repeat it).  All loads are
     // unconditional (clamped at the end), so the loads-in-flight count
     // between a load and its use is static.
     u32x4_t buf[PD][R];
-    u32x4_t xbuf[PD];
+    u32x4_t xbuf[PD][NBR];
     u32x2_t sbuf[PD];
     u32x2_t zbuf[ASYM ? PD : 1];
     int ps = 0, pt = 0;  // next step to prefetch
@@ -163,7 +181,10 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
             t = T - 1;
         }
         const int set = w + s * W;
-        xbuf[j] = reinterpret_cast<const u32x4_t *>(x)[min(set * 64 + lane, xchunks - 1)];
+        const int xc = min(set * 64 + lane, xchunks - 1);
+#pragma unroll
+        for (int b = 0; b < NBR; ++b)
+            xbuf[j][b] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(b, batch - 1) * ldx)[xc];
         const int g = min(4 * set + gg, G - 1);
         const uint8_t *c = planes + (((int64_t)(t_begin + t) * G + g) * 16 + i) * 16;
 #pragma unroll
@@ -186,35 +207,52 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         for (int j = 0; j < PD; ++j) load_step(j);
     }
 
-    uint32_t X2[64];              // A operand: the lane's group of X if i == gg, else zeros
-    float corr[4] = {0.f, 0.f, 0.f, 0.f};   // the set's group corrections (wave-uniform)
-    float sgv[4] = {0.f, 0.f, 0.f, 0.f};    // the set's group sums of X (asymmetric term)
+    uint32_t X2[64];  // A operand: group gg of batch row i / 4's X if i % 4 == gg, else zeros
+    // the set's group corrections and group sums of X (asymmetric term), for
+    // the batch row of the lane's outputs (wave-uniform at NBR = 1)
+    float corr[4] = {0.f, 0.f, 0.f, 0.f};
+    float sgv[4] = {0.f, 0.f, 0.f, 0.f};
     int cs = 0, ct = 0;  // step being computed
     auto compute = [&](int j) {
         const int set = w + cs * W;
         if (ct == 0) {
             // New set: stage its X (LDS operations of one wave complete in
             // order, so the previous set's reads are done), read back this
-            // lane's A operand, and form each group's correction over its
-            // quarter of the wave.
-            reinterpret_cast<u32x4_t *>(xw)[lane] = xbuf[j];
-            const uint32_t *src = (i == gg) ? xw + 64 * gg : zblk;
+            // lane's A operand, and form each group's correction over 16
+            // lanes (lane i takes the pairs i, i+16, i+32, i+48 of a group).
+#pragma unroll
+            for (int b = 0; b < NBR; ++b) reinterpret_cast<u32x4_t *>(xw + 256 * b)[lane] = xbuf[j][b];
+            const uint32_t *src = (NBR > 1 ? (i & 3) == gg : i == gg) ? xw + 256 * (i >> 2) + 64 * gg : zblk;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const u32x4_t v = reinterpret_cast<const u32x4_t *>(src)[q];
                 X2[4 * q] = v.x; X2[4 * q + 1] = v.y; X2[4 * q + 2] = v.z; X2[4 * q + 3] = v.w;
             }
             const uint32_t one = 0x3F803F80u;  // bf16 (1.0, 1.0)
-            float sx = 0.f;
+            if constexpr (NBR == 1) {
+                // quarter gg forms group gg's sums; every lane takes all four
+                float sx = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sx = dot2(one, xw[64 * gg + i + 16 * q], sx);
-            const float cg = row16_sum(my_coef * sx);
-            float sg = 0.f;
-            if constexpr (ASYM) sg = row16_sum(sx);
+                for (int q = 0; q < 4; ++q) sx = dot2(one, xw[64 * gg + i + 16 * q], sx);
+                const float cg = row16_sum(my_coef * sx);
+                float sg = 0.f;
+                if constexpr (ASYM) sg = row16_sum(sx);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                corr[v] = lane_value(cg, 16 * v);
-                if constexpr (ASYM) sgv[v] = lane_value(sg, 16 * v);
+                for (int v = 0; v < 4; ++v) {
+                    corr[v] = lane_value(cg, 16 * v);
+                    if constexpr (ASYM) sgv[v] = lane_value(sg, 16 * v);
+                }
+            } else {
+                // quarter gg forms the four group sums of batch row gg, the
+                // row of its outputs
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float sx = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sx = dot2(one, xw[256 * gg + 64 * v + i + 16 * q], sx);
+                    corr[v] = row16_sum(my_coef * sx);
+                    if constexpr (ASYM) sgv[v] = row16_sum(sx);
+                }
             }
         }
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -239,8 +277,9 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
                 }
             }
         }
-        // lane (i, 0): acc[v] = group 4*set + v of row i (lanes of the other
-        // quarters hold the zero rows of A)
+        // lane (i, b): acc[v] = group 4*set + v of weight row i for batch
+        // row b (at NBR = 1 the lanes of quarters 1..3 hold the zero rows of
+        // A; batch rows past the last are computed and dropped)
         const int row = 16 * (t_begin + ct) + i;
         const bool rvalid = row < n;
         float out = 0.f;
@@ -262,13 +301,13 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
         }
         return out;
     };
-    // Accumulate into this row's own LDS slot for the tile.  Each slot has a
-    // single writer (lane i of quarter 0), so no atomic is needed and the
-    // order of the additions is fixed: the wave's first set stores, later
-    // sets read, add and store.
+    // Accumulate into this output's own LDS slot for the tile.  Each slot
+    // has a single writer (lane i of quarter 0 at NBR = 1, else every lane),
+    // so no atomic is needed and the order of the additions is fixed: the
+    // wave's first set stores, later sets read, add and store.
     auto commit = [&](float v) {
-        if (gg == 0) {
-            float *slot = &red[(w * slots + ct) * 16 + i];
+        if (NBR > 1 || gg == 0) {
+            float *slot = &red[(w * slots + ct) * RW + (NBR > 1 ? lane : i)];
             if (cs == 0)
                 *slot = v;
             else
@@ -304,15 +343,15 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x,
     for (int j = 0; j < PD; ++j)  // the last < PD steps are already loaded
         if (Ufull + j < U) commit(compute(j));
 
-    // Rows: add the waves, in a fixed order.
+    // Outputs: add the waves, in a fixed order.
     __syncthreads();
     const float post = (float)(1 << (8 - R));
-    for (int e = threadIdx.x; e < T * 16; e += blockDim.x) {
-        const int t = e >> 4, ii = e & 15;
+    for (int e = threadIdx.x; e < T * RW; e += blockDim.x) {
+        const int t = e / RW, l = e % RW;
+        const int b = l >> 4, row = 16 * (t_begin + t) + (l & 15);
         float sum = 0.f;
-        for (int ww = 0; ww < W; ++ww) sum += red[(ww * slots + t) * 16 + ii];
-        const int row = 16 * t_begin + e;
-        if (row < n) store_y(y, ybf16, row, sum * post);
+        for (int ww = 0; ww < W; ++ww) sum += red[(ww * slots + t) * RW + l];
+        if (row < n && b < batch) store_y(y, ybf16, (int64_t)b * ldy + row, sum * post);
     }
 }
 
@@ -389,31 +428,35 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
     }
 }
 
-template <int R, int PD, bool ASYM>
+// grid: ceil(tiles / tiles_per_wg); batch rows 1..NBR of x (row stride ldx)
+// and y (row stride ldy).
+template <int R, int PD, bool ASYM, int NBR>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_kernel(const uint16_t *__restrict__ x,
+                                                                  int64_t ldx, int batch,
                                                                   const uint8_t *__restrict__ planes,
                                                                   int64_t plane_bytes,
                                                                   const uint16_t *__restrict__ scales,
                                                                   const uint16_t *__restrict__ zeros,
                                                                   int n, int k, int tiles_total,
                                                                   int tiles_per_wg,
-                                                                  float *__restrict__ y, int ybf16) {
+                                                                  float *__restrict__ y, int64_t ldy,
+                                                                  int ybf16) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int t_begin = blockIdx.x * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    gemv_tiles<R, PD, ASYM>(x, planes, plane_bytes, scales, zeros, n, k, t_begin, T, tiles_per_wg,
-                            y, ybf16, lds);
+    gemv_tiles<R, PD, ASYM, NBR>(x, ldx, batch, planes, plane_bytes, scales, zeros, n, k, t_begin, T,
+                                 tiles_per_wg, y, ldy, ybf16, lds);
 }
 
 // ---------------------------------------------------------------- grouped launch
 
 struct GemvJob {
-    const uint16_t *x;
+    const uint16_t *x;  // [batch][k], y [batch][n]
     const uint8_t *planes;
     int64_t plane_bytes;
     const uint16_t *scales;
     float *y;
-    int n, k, r, tiles, tpw, item_begin;
+    int batch, n, k, r, tiles, tpw, item_begin;
 };
 
 struct GemvGroup {
@@ -423,6 +466,8 @@ struct GemvGroup {
 
 // Workgroup b runs item b; items are numbered product by product.  Every
 // item has `slots` partial-sum slots per wave (the largest tpw of the group).
+// NBR = 1: batch-1 products; NBR = 4: batch 2..4.
+template <int NBR>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_group_kernel(GemvGroup grp) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int item = blockIdx.x;
@@ -434,8 +479,9 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_gro
     switch (J.r) {
 #define NBW_GEMV_CASE(RR)                                                                    \
     case RR:                                                                                 \
-        gemv_tiles<RR, gemv_depth(RR), false>(J.x, J.planes, J.plane_bytes, J.scales, nullptr,   \
-                                              J.n, J.k, t_begin, T, grp.slots, J.y, 0, lds);  \
+        gemv_tiles<RR, gemv_depth(RR), false, NBR>(J.x, J.k, J.batch, J.planes, J.plane_bytes,   \
+                                                   J.scales, nullptr, J.n, J.k, t_begin, T,      \
+                                                   grp.slots, J.y, J.n, 0, lds);                 \
         break;
         NBW_GEMV_CASE(1)
         NBW_GEMV_CASE(2)
@@ -475,38 +521,51 @@ static GemvPlan gemv_plan(int n, int k, int r, int cu_count) {
 
 static bool gemv_streamable(int k);
 
-template <int R, bool ASYM>
+template <int R, bool ASYM, int NBR>
 static void launch_stream(const GemvPlan &p, int tiles, const QgemmArgs &a, const uint16_t *x,
-                          float *y, hipStream_t stream) {
+                          int nb, float *y, hipStream_t stream) {
     const dim3 grid((tiles + p.tpw - 1) / p.tpw), block(64 * p.waves);
-    const size_t lds = gemv_lds_bytes(p.waves, p.tpw);
+    const size_t lds = gemv_lds_bytes(p.waves, p.tpw, NBR);
     if (p.deep)
-        hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R), ASYM>), grid, block, lds, stream, x, a.planes,
-                           a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, p.tpw, y, a.ybf16);
+        hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R), ASYM, NBR>), grid, block, lds, stream, x,
+                           a.ldx, nb, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles,
+                           p.tpw, y, a.ldy, a.ybf16);
     else
-        hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT, ASYM>), grid, block, lds, stream, x,
-                           a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles, p.tpw, y,
-                           a.ybf16);
+        hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT, ASYM, NBR>), grid, block, lds, stream, x,
+                           a.ldx, nb, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles,
+                           p.tpw, y, a.ldy, a.ybf16);
 }
 
 template <int R>
 static void launch_r(const QgemmArgs &a, int cu_count, hipStream_t stream) {
     const int tiles = (a.n + 15) / 16;
-    for (int64_t b = 0; b < a.batch; ++b) {  // one batch row per launch
+    const bool stream_k = gemv_streamable(a.k);
+    // Up to GEMV_MAX_BATCH batch rows per launch of the streaming kernel
+    // (one per launch of the odd-group-count kernel).
+    for (int64_t b = 0; b < a.batch;) {
+        const int nb = stream_k ? (int)std::min<int64_t>(GEMV_MAX_BATCH, a.batch - b) : 1;
         const uint16_t *x = a.x + b * a.ldx;
         // (y advances by ldy elements of the output type)
         float *y = a.ybf16 ? reinterpret_cast<float *>(reinterpret_cast<uint16_t *>(a.y) + b * a.ldy)
                            : a.y + b * a.ldy;
-        if (!gemv_streamable(a.k)) {
+        if (!stream_k) {
             hipLaunchKernelGGL(gemv_odd_kernel<R>, dim3(tiles), dim3(64 * GEMV_ODD_WAVES), 0, stream,
                                x, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, y, a.ybf16);
         } else {
             const GemvPlan p = gemv_plan(a.n, a.k, R, cu_count);
-            if (a.zeros)
-                launch_stream<R, true>(p, tiles, a, x, y, stream);
-            else
-                launch_stream<R, false>(p, tiles, a, x, y, stream);
+            if (nb == 1) {
+                if (a.zeros)
+                    launch_stream<R, true, 1>(p, tiles, a, x, 1, y, stream);
+                else
+                    launch_stream<R, false, 1>(p, tiles, a, x, 1, y, stream);
+            } else {
+                if (a.zeros)
+                    launch_stream<R, true, GEMV_MAX_BATCH>(p, tiles, a, x, nb, y, stream);
+                else
+                    launch_stream<R, false, GEMV_MAX_BATCH>(p, tiles, a, x, nb, y, stream);
+            }
         }
+        b += nb;
     }
 }
 
@@ -529,49 +588,64 @@ void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
     if (!gemv_streamable(a.k)) {
         snprintf(out, len, "nbw::gemv_odd_kernel<%d>", r);
     } else {
+        // (the kernel of the first launch: batch rows 1..4)
         const GemvPlan p = gemv_plan(a.n, a.k, r, cu_count);
-        snprintf(out, len, "nbw::gemv_kernel<%d, %d, %s>", r, p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT,
-                 a.zeros ? "true" : "false");
+        snprintf(out, len, "nbw::gemv_kernel<%d, %d, %s, %d>", r, p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT,
+                 a.zeros ? "true" : "false", a.batch > 1 ? GEMV_MAX_BATCH : 1);
     }
 }
 
 int gemv_group_capacity() { return GEMV_MAX_GROUP; }
+int gemv_max_batch() { return GEMV_MAX_BATCH; }
 
 // The streaming kernel reads the scales of a set's four groups as one aligned
 // 8-byte word: it takes group counts that are multiples of 4 (every other
 // shape goes to the plain one-tile kernel).
 static bool gemv_streamable(int k) { return ((k / 128) & 3) == 0; }
 
+// (contiguous rows: x [batch][k], y [batch][n])
 bool gemv_group_eligible(const QgemmArgs &a) {
-    return a.batch == 1 && gemv_streamable(a.k) && !a.zeros && !a.ybf16;
+    return a.batch >= 1 && a.batch <= GEMV_MAX_BATCH && gemv_streamable(a.k) && !a.zeros && !a.ybf16;
 }
 
+// One launch per kernel variant: the batch-1 products, then those of batch
+// 2..4, each in the order given.
 hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
                              hipStream_t stream) {
-    GemvGroup grp = {};
-    grp.count = count;
-    int items = 0, slots = 1;
-    for (int j = 0; j < count; ++j) {
-        const QgemmArgs &a = probs[j];
-        GemvJob &J = grp.job[j];
-        J.x = a.x;
-        J.planes = a.planes;
-        J.plane_bytes = a.plane_bytes;
-        J.scales = a.scales;
-        J.y = a.y;
-        J.n = a.n;
-        J.k = a.k;
-        J.r = rs[j];
-        J.tiles = (a.n + 15) / 16;
-        J.tpw = gemv_plan(a.n, a.k, rs[j], cu_count).tpw;
-        if (J.tpw > slots) slots = J.tpw;
-        J.item_begin = items;
-        items += (J.tiles + J.tpw - 1) / J.tpw;
+    for (int nbr : {1, GEMV_MAX_BATCH}) {
+        GemvGroup grp = {};
+        int items = 0, slots = 1;
+        for (int j0 = 0; j0 < count; ++j0) {
+            const QgemmArgs &a = probs[j0];
+            if ((a.batch > 1 ? GEMV_MAX_BATCH : 1) != nbr) continue;
+            GemvJob &J = grp.job[grp.count++];
+            J.x = a.x;
+            J.planes = a.planes;
+            J.plane_bytes = a.plane_bytes;
+            J.scales = a.scales;
+            J.y = a.y;
+            J.batch = (int)a.batch;
+            J.n = a.n;
+            J.k = a.k;
+            J.r = rs[j0];
+            J.tiles = (a.n + 15) / 16;
+            J.tpw = gemv_plan(a.n, a.k, rs[j0], cu_count).tpw;
+            if (J.tpw > slots) slots = J.tpw;
+            J.item_begin = items;
+            items += (J.tiles + J.tpw - 1) / J.tpw;
+        }
+        if (grp.count == 0) continue;
+        grp.slots = slots;
+        if (nbr == 1)
+            hipLaunchKernelGGL(gemv_group_kernel<1>, dim3(items), dim3(64 * GEMV_MAX_WAVES),
+                               gemv_lds_bytes(GEMV_MAX_WAVES, slots, 1), stream, grp);
+        else
+            hipLaunchKernelGGL(gemv_group_kernel<GEMV_MAX_BATCH>, dim3(items), dim3(64 * GEMV_MAX_WAVES),
+                               gemv_lds_bytes(GEMV_MAX_WAVES, slots, GEMV_MAX_BATCH), stream, grp);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    grp.slots = slots;
-    hipLaunchKernelGGL(gemv_group_kernel, dim3(items), dim3(64 * GEMV_MAX_WAVES),
-                       gemv_lds_bytes(GEMV_MAX_WAVES, slots), stream, grp);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace nbw

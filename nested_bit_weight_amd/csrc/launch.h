@@ -70,6 +70,7 @@ hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hi
 // Grouped batch-1 launch: several products (each with its own r) as one
 // dispatch.  Eligible problems: batch 1, shapes the streaming kernel takes.
 int gemv_group_capacity();
+int gemv_max_batch();  // batch rows one streaming launch takes
 bool gemv_group_eligible(const QgemmArgs &a);
 hipError_t launch_gemv_group(const QgemmArgs *probs, const int *rs, int count, int cu_count,
                              hipStream_t stream);

@@ -85,10 +85,13 @@ def test_smallb_set_boundaries_asym(nbw, case, batch):
     assert e <= CONTRACT and e <= DESIGN_BOUND
 
 
-# The automatic choice: the small-batch kernel while it needs one pass over the
-# planes (32 batch rows a pass for r <= 4 on short tile runs, 16 otherwise), or
-# two passes with k <= 8192; the large-batch GEMM beyond.
+# The automatic choice: the streaming kernel up to batch 4; the small-batch
+# kernel while it needs one pass over the planes (32 batch rows a pass for
+# r <= 4 on short tile runs, 16 otherwise), or two passes with k <= 8192; the
+# large-batch GEMM beyond.
 @pytest.mark.parametrize("batch,k,r,family", [
+    (2, 1024, 3, "gemv"), (4, 1024, 6, "gemv"), (4, 8320, 2, "gemv"), (5, 1024, 3, "smallb"),
+    (5, 8320, 6, "smallb"),
     (17, 1024, 3, "smallb"), (32, 1024, 3, "smallb"), (33, 1024, 3, "smallb"), (64, 1024, 3, "smallb"),
     (65, 1024, 3, "gemm"), (32, 8320, 3, "smallb"), (33, 8320, 3, "gemm"),
     (17, 1024, 6, "smallb"), (32, 1024, 6, "smallb"), (33, 1024, 6, "gemm"), (17, 8320, 6, "gemm")])
