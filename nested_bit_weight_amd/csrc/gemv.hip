@@ -93,6 +93,19 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// A wave-uniform global address, pinned to scalar registers: a load from it
+// plus a 32-bit lane offset then takes the scalar-base addressing form (no
+// 64-bit vector address arithmetic), which the compiler otherwise loses when
+// it folds the lane offset in before a uniform plane offset.  Loads go
+// through global (address space 1) pointers, not flat ones.
+template <class T> using gptr = const __attribute__((address_space(1))) T *;
+__device__ __forceinline__ uint64_t uniform_addr(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ float lane_value(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -120,7 +133,11 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // stream), stages it in its own 1 KB of LDS and reads back its lanes' A
 // operands, so no barrier -- and no wait for every load in flight -- stands
 // between a wave's first loads and its first step.
-template <int R, int PD, bool ASYM, int NBR>
+//
+// XO: load a set's X only with its first tile (runs of 3 or more tiles per
+// workgroup, where the reloads' memory-pipe traffic costs more than the
+// looser load-wait counts that a conditional load leaves).
+template <int R, int PD, bool ASYM, int NBR, bool XO>
 __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64_t ldx, int batch,
                                            const uint8_t *__restrict__ planes,
                                            int64_t plane_bytes,
@@ -164,16 +181,23 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
     // Step loads: R plane chunks (row i, group 4*set + gg), the two aligned
     // 32-bit words of the scales of row i's four groups of the set, and the
     // lane's 16 bytes of the set's X of each batch row (the same chunks for
-    // every tile of a set; reloading them keeps the number of loads per step
-    // fixed; batch rows past the last repeat it).  All loads are
-    // unconditional (clamped at the end), so the loads-in-flight count
-    // between a load and its use is static.
+    // every tile of a set; batch rows past the last repeat it).  Unless XO,
+    // all loads are unconditional (X reloaded with every tile, steps past the
+    // end clamped), so the loads-in-flight count between a load and its use
+    // is static.
     u32x4_t buf[PD][R];
     u32x4_t xbuf[PD][NBR];
     u32x2_t sbuf[PD];
     u32x2_t zbuf[ASYM ? PD : 1];
     int ps = 0, pt = 0;  // next step to prefetch
-    const int xchunks = k >> 3;
+    // Every address of a step is a wave-uniform base (scalar arithmetic) plus
+    // a per-lane offset fixed for the whole kernel: with k/128 a multiple of
+    // 4, the chunk of (row i, group 4*set + gg) of a tile lies lane*16 bytes
+    // into the tile's run of the set's chunks, and the lane's X lies lane*16
+    // bytes into the set's 1 KB.  Only the scales' row needs a clamp (the
+    // padding rows of a ragged last tile read row n-1's, and are dropped).
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    const uint32_t srow = (uint32_t)i * (uint32_t)G * 2u;  // row i's scales, bytes into a tile's
     auto load_step = [&](int j) {
         int s = ps, t = pt;
         if (s >= my_sets) {
@@ -181,22 +205,29 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
             t = T - 1;
         }
         const int set = w + s * W;
-        const int xc = min(set * 64 + lane, xchunks - 1);
+        const int tile = t_begin + t;
+        // (a fresh copy of the lane offset in each step: the compiler
+        // otherwise hoists its 64-bit extension out of the loop and then
+        // adds it to the base with vector arithmetic)
+        uint32_t lo16 = lane16;
+        asm volatile("" : "+v"(lo16));
 #pragma unroll
-        for (int b = 0; b < NBR; ++b)
-            xbuf[j][b] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(b, batch - 1) * ldx)[xc];
-        const int g = min(4 * set + gg, G - 1);
-        const uint8_t *c = planes + (((int64_t)(t_begin + t) * G + g) * 16 + i) * 16;
+        for (int b = 0; b < NBR; ++b) {
+            const uint64_t xs = uniform_addr(reinterpret_cast<const uint8_t *>(x + (int64_t)min(b, batch - 1) * ldx) +
+                                             (int64_t)set * 1024);
+            if (!XO || t == 0) xbuf[j][b] = *(gptr<u32x4_t>)(xs + lo16);
+        }
+        const uint8_t *c = planes + ((int64_t)tile * G + 4 * set) * 256;
 #pragma unroll
         for (int p = 0; p < R; ++p)
-            buf[j][p] =
-                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(c + p * plane_bytes));
-        // groups 4*set .. 4*set+3 of row i: one aligned 8-byte word (k/128 is
-        // a multiple of 4)
-        const int row = min(16 * (t_begin + t) + i, n - 1);
-        const int64_t r0 = (int64_t)row * G + 4 * set;
-        sbuf[j] = *reinterpret_cast<const u32x2_t *>(scales + r0);
-        if constexpr (ASYM) zbuf[j] = *reinterpret_cast<const u32x2_t *>(zeros + r0);
+            buf[j][p] = __builtin_nontemporal_load((gptr<u32x4_t>)(uniform_addr(c + (int64_t)p * plane_bytes) + lo16));
+        // groups 4*set .. 4*set+3 of row min(16 tile + i, n - 1): one aligned
+        // 8-byte word
+        const int64_t sb = ((int64_t)16 * tile * G + 4 * set) * 2;
+        const uint32_t so = min(srow, (uint32_t)(n - 1 - 16 * tile) * (uint32_t)G * 2u);
+        sbuf[j] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint8_t *>(scales) + sb + so);
+        if constexpr (ASYM)
+            zbuf[j] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint8_t *>(zeros) + sb + so);
         if (++pt == T) {
             pt = 0;
             ++ps;
@@ -280,14 +311,14 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
         // lane (i, b): acc[v] = group 4*set + v of weight row i for batch
         // row b (at NBR = 1 the lanes of quarters 1..3 hold the zero rows of
         // A; batch rows past the last are computed and dropped)
-        const int row = 16 * (t_begin + ct) + i;
-        const bool rvalid = row < n;
+        // (rows past n of a ragged last tile carry row n-1's scales and are
+        // never stored)
         float out = 0.f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const uint32_t wd = (v >> 1) ? sbuf[j].y : sbuf[j].x;
             const uint32_t sbits = (v & 1) ? (wd & 0xFFFF0000u) : (wd << 16);
-            const float s = rvalid ? __uint_as_float(sbits) : 0.f;
+            const float s = __uint_as_float(sbits);
             float term = acc[v] + corr[v];
             if constexpr (ASYM) {
                 // asymmetric child = symmetric child + s * (127.5 - z) per
@@ -430,7 +461,7 @@ __global__ __launch_bounds__(256) void gemv_odd_kernel(const uint16_t *__restric
 
 // grid: ceil(tiles / tiles_per_wg); batch rows 1..NBR of x (row stride ldx)
 // and y (row stride ldy).
-template <int R, int PD, bool ASYM, int NBR>
+template <int R, int PD, bool ASYM, int NBR, bool XO>
 __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_kernel(const uint16_t *__restrict__ x,
                                                                   int64_t ldx, int batch,
                                                                   const uint8_t *__restrict__ planes,
@@ -444,7 +475,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_ker
     extern __shared__ __align__(16) unsigned char lds[];
     const int t_begin = blockIdx.x * tiles_per_wg;
     const int T = min(tiles_per_wg, tiles_total - t_begin);
-    gemv_tiles<R, PD, ASYM, NBR>(x, ldx, batch, planes, plane_bytes, scales, zeros, n, k, t_begin, T,
+    gemv_tiles<R, PD, ASYM, NBR, XO>(x, ldx, batch, planes, plane_bytes, scales, zeros, n, k, t_begin, T,
                                  tiles_per_wg, y, ldy, ybf16, lds);
 }
 
@@ -479,7 +510,7 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_gro
     switch (J.r) {
 #define NBW_GEMV_CASE(RR)                                                                    \
     case RR:                                                                                 \
-        gemv_tiles<RR, gemv_depth(RR), false, NBR>(J.x, J.k, J.batch, J.planes, J.plane_bytes,   \
+        gemv_tiles<RR, gemv_depth(RR), false, NBR, false>(J.x, J.k, J.batch, J.planes, J.plane_bytes,   \
                                                    J.scales, nullptr, J.n, J.k, t_begin, T,      \
                                                    grp.slots, J.y, J.n, 0, lds);                 \
         break;
@@ -502,7 +533,11 @@ __global__ __launch_bounds__(64 * GEMV_MAX_WAVES, GEMV_WGS_PER_CU) void gemv_gro
 struct GemvPlan {
     int waves, tpw;
     bool deep;  // prefetch depth gemv_depth(r), else GEMV_DEPTH_SHORT
+    bool xo;    // (deep only) each set's X loaded with its first tile only
 };
+
+// Tile runs from which a set's X is loaded once, not with every tile.
+constexpr int GEMV_XO_MIN_TILES = 3;
 
 static GemvPlan gemv_plan(int n, int k, int r, int cu_count) {
     const int tiles = (n + 15) / 16;
@@ -516,6 +551,7 @@ static GemvPlan gemv_plan(int n, int k, int r, int cu_count) {
     const int nsets = (k / 128 + 3) / 4;
     const int steps = (nsets + p.waves - 1) / p.waves * tpw;  // per wave, at most
     p.deep = gemv_depth(r) > GEMV_DEPTH_SHORT && steps >= 4;
+    p.xo = p.deep && tpw >= GEMV_XO_MIN_TILES;
     return p;
 }
 
@@ -526,13 +562,17 @@ static void launch_stream(const GemvPlan &p, int tiles, const QgemmArgs &a, cons
                           int nb, float *y, hipStream_t stream) {
     const dim3 grid((tiles + p.tpw - 1) / p.tpw), block(64 * p.waves);
     const size_t lds = gemv_lds_bytes(p.waves, p.tpw, NBR);
-    if (p.deep)
-        hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R), ASYM, NBR>), grid, block, lds, stream, x,
+    if (p.deep && p.xo)
+        hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R), ASYM, NBR, true>), grid, block, lds, stream, x,
+                           a.ldx, nb, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles,
+                           p.tpw, y, a.ldy, a.ybf16);
+    else if (p.deep)
+        hipLaunchKernelGGL((gemv_kernel<R, gemv_depth(R), ASYM, NBR, false>), grid, block, lds, stream, x,
                            a.ldx, nb, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles,
                            p.tpw, y, a.ldy, a.ybf16);
     else
-        hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT, ASYM, NBR>), grid, block, lds, stream, x,
-                           a.ldx, nb, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles,
+        hipLaunchKernelGGL((gemv_kernel<R, GEMV_DEPTH_SHORT, ASYM, NBR, false>), grid, block, lds, stream,
+                           x, a.ldx, nb, a.planes, a.plane_bytes, a.scales, a.zeros, a.n, a.k, tiles,
                            p.tpw, y, a.ldy, a.ybf16);
 }
 
@@ -590,8 +630,9 @@ void gemv_name(int r, const QgemmArgs &a, int cu_count, char *out, size_t len) {
     } else {
         // (the kernel of the first launch: batch rows 1..4)
         const GemvPlan p = gemv_plan(a.n, a.k, r, cu_count);
-        snprintf(out, len, "nbw::gemv_kernel<%d, %d, %s, %d>", r, p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT,
-                 a.zeros ? "true" : "false", a.batch > 1 ? GEMV_MAX_BATCH : 1);
+        snprintf(out, len, "nbw::gemv_kernel<%d, %d, %s, %d, %s>", r,
+                 p.deep ? gemv_depth(r) : GEMV_DEPTH_SHORT, a.zeros ? "true" : "false",
+                 a.batch > 1 ? GEMV_MAX_BATCH : 1, p.xo ? "true" : "false");
     }
 }
 
