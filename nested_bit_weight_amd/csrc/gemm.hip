@@ -41,7 +41,6 @@
 namespace nbw {
 
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int GEMM_BM = 128;        // batch rows per workgroup
 constexpr int GEMM_WAVES = 8;       // waves per workgroup, one 32-row weight block each

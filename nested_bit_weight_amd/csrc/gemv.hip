@@ -37,7 +37,6 @@
 
 namespace nbw {
 
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int GEMV_MAX_WAVES = 8;   // waves per workgroup (the launch picks 4 or 8)
 constexpr int GEMV_ODD_WAVES = 4;   // waves per workgroup of the odd-group-count kernel
