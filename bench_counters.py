@@ -58,10 +58,14 @@ PROBES = {
                       ("gemv.hip", "decode.h"),
                       [(L70, "gate_up", 1, 3), (L70, "gate_up", 1, 2), (L70, "down", 1, 3),
                        (L70, "down", 1, 2), (QWEN, "gate_up", 1, 6), (QWEN, "gate_up", 1, 4)]),
-    "smallb_b16": ("small-batch MFMA kernel on the Llama-3.1-8B linears (batch 16 at r = 4, 2; batch 4 at r = 4)",
+    "gemv_b4": ("streaming kernel with four batch rows per launch on the Llama-3.1-8B linears (the batch-4 "
+                "step: r = 4, 3, 2)",
+                ("gemv.hip", "decode.h"),
+                [(LLAMA, lin, 4, r) for r in (4, 3, 2) for lin in ("qkv", "o", "gate_up", "down")]),
+    "smallb_b16": ("small-batch MFMA kernel on the Llama-3.1-8B linears (batch 16 at r = 4, 2; batch 8 at r = 4)",
                    ("smallb.hip", "decode.h"),
                    [(LLAMA, lin, 16, r) for r in (4, 2) for lin in ("qkv", "o", "gate_up", "down")]
-                   + [(LLAMA, lin, 4, 4) for lin in ("qkv", "o", "gate_up", "down")]),
+                   + [(LLAMA, lin, 8, 4) for lin in ("qkv", "o", "gate_up", "down")]),
     "gemm_b256": ("large-batch GEMM on the Llama-3.1-8B linears (batch 256 at r = 8, 4)",
                   ("gemm_wide.hip", "gemm.hip", "decode.h"),
                   [(LLAMA, lin, 256, r) for r in (8, 4) for lin in ("qkv", "o", "gate_up", "down")]),

@@ -415,9 +415,10 @@ def qgemm_grouped(items, outs=None):
     """Several products in as few dispatches as possible.
 
     ``items``: sequence of ``(x, w, scales, r)`` as for :func:`qgemm`.  Returns the
-    fp32 outputs (or fills ``outs``).  Batch-1 products run as one grouped launch of
-    the streaming kernel, batch-2..16 products (k/128 a multiple of 4) as one of the
-    small-batch kernel; the rest one by one."""
+    fp32 outputs (or fills ``outs``).  Batch 1..4 products run as grouped launches of
+    the streaming kernel (one for batch 1, one for batch 2..4), batch-5..16 products
+    as one of the small-batch kernel (k/128 a multiple of 4 for both); the rest one
+    by one."""
     items = list(items)
     if outs is None:
         outs = [None] * len(items)
