@@ -66,16 +66,22 @@ constexpr int GEMV_MAX_BATCH = 4;
 // groups x 128 bf16 a row, each group padded by 16 bytes) and a run of zeros,
 // then the partial sums fp32 [W][slots][16 NBR], one slot per tile.
 // In one A-operand load a few lanes of each quarter read a group and the rest
-// read zeros.  Bank offsets (words mod 64, and mod 32): group g of row b sits
-// at 16 b + 4 g, so the active lanes of quarter g (rows 0..3 of group g) hit
-// 4 g + 16 b; quarter g's zero lanes read at offset 4 g + 8 of the zero run,
-// a bank that no active lane of that quarter uses.  (A shared zero block at
-// one offset made every A-operand load of a set switch conflict.)
-constexpr int GEMV_XGROUP = 68;               // words per staged group (64 + pad)
-constexpr int GEMV_XROW = 4 * GEMV_XGROUP;    // words per staged batch row
+// read zeros; quarter g's zero lanes read at offset 4 g + 8 of the zero run.
+// Bank offsets (words mod 64, and mod 32):
+//  - NBR = 4: groups 68 words apart, rows 272: group g of row b at 16 b + 4 g,
+//    so the four active lanes of quarter g (rows 0..3 of group g) hit
+//    4 g + 16 b, none of them at 4 g + 8; the correction reads (lane (i, b):
+//    word i + 16 q of group v of row b) hit 16 b + 4 v + i, distinct.
+//  - NBR = 1: groups 80 words apart: the active lane of quarter g reads at
+//    16 g, its zero lanes at 4 g + 8; the correction reads (lane (i, g): word
+//    i + 16 q of group g) hit 16 g + i, distinct.
+// (A shared zero block at one offset made every A-operand load of a set
+// switch conflict.)
+__host__ __device__ constexpr int gemv_xgroup(int nbr) { return nbr > 1 ? 68 : 80; }  // words
+__host__ __device__ constexpr int gemv_xrow(int nbr) { return 4 * gemv_xgroup(nbr); }
 __host__ __device__ constexpr int gemv_round64(int v) { return (v + 63) / 64 * 64; }
 // zero run (words from the wave's base; a multiple of 64): 8 + 12 + 64 words used
-__host__ __device__ constexpr int gemv_zoff(int nbr) { return gemv_round64(GEMV_XROW * nbr); }
+__host__ __device__ constexpr int gemv_zoff(int nbr) { return gemv_round64(gemv_xrow(nbr) * nbr); }
 __host__ __device__ constexpr int gemv_wave_lds(int nbr) { return 4 * gemv_round64(gemv_zoff(nbr) + 96); }
 __host__ __device__ constexpr size_t gemv_lds_bytes(int waves, int slots, int nbr) {
     return (size_t)waves * gemv_wave_lds(nbr) + (size_t)waves * slots * 16 * nbr * 4;
@@ -164,8 +170,9 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int i = lane & 15, gg = lane >> 4;
-    // this wave's set of X, group g of batch row b at xw + GEMV_XROW b +
-    // GEMV_XGROUP g; then the zero run, read by quarter g at offset 4 g + 8
+    // this wave's set of X, group g of batch row b at xw + XROW b + XGROUP g;
+    // then the zero run, read by quarter g at offset 4 g + 8
+    constexpr int XGROUP = gemv_xgroup(NBR), XROW = gemv_xrow(NBR);
     uint32_t *xw = reinterpret_cast<uint32_t *>(lds + (size_t)w * gemv_wave_lds(NBR));
     uint32_t *zrun = xw + gemv_zoff(NBR);
     const uint32_t *zblk = zrun + 8 + 4 * gg;
@@ -266,9 +273,9 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
             // lanes (lane i takes the pairs i, i+16, i+32, i+48 of a group).
 #pragma unroll
             for (int b = 0; b < NBR; ++b)  // (lane l holds words 4l..4l+3 of the set: group l / 16)
-                *reinterpret_cast<u32x4_t *>(xw + GEMV_XROW * b + GEMV_XGROUP * gg + 4 * i) = xbuf[j][b];
+                *reinterpret_cast<u32x4_t *>(xw + XROW * b + XGROUP * gg + 4 * i) = xbuf[j][b];
             const uint32_t *src = (NBR > 1 ? (i & 3) == gg : i == gg)
-                                      ? xw + GEMV_XROW * (i >> 2) + GEMV_XGROUP * gg : zblk;
+                                      ? xw + XROW * (i >> 2) + XGROUP * gg : zblk;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const u32x4_t v = reinterpret_cast<const u32x4_t *>(src)[q];
@@ -279,7 +286,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
                 // quarter gg forms group gg's sums; every lane takes all four
                 float sx = 0.f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sx = dot2(one, xw[GEMV_XGROUP * gg + i + 16 * q], sx);
+                for (int q = 0; q < 4; ++q) sx = dot2(one, xw[XGROUP * gg + i + 16 * q], sx);
                 const float cg = row16_sum(my_coef * sx);
                 float sg = 0.f;
                 if constexpr (ASYM) sg = row16_sum(sx);
@@ -296,7 +303,7 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
                     float sx = 0.f;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        sx = dot2(one, xw[GEMV_XROW * gg + GEMV_XGROUP * v + i + 16 * q], sx);
+                        sx = dot2(one, xw[XROW * gg + XGROUP * v + i + 16 * q], sx);
                     corr[v] = row16_sum(my_coef * sx);
                     if constexpr (ASYM) sgv[v] = row16_sum(sx);
                 }
