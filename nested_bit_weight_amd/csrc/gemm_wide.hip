@@ -44,6 +44,7 @@
 //  - where the output tiles leave CUs idle, k splits over workgroups into a
 //    caller workspace and a second launch adds the splits in order.
 #include <cstdio>
+#include <type_traits>
 
 #include "decode.h"
 #include "launch.h"
@@ -244,6 +245,17 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
         }
     };
 
+    // Two teams of waves (r <= 4): team A decodes a group's weights at the
+    // group's start, team B right after its chains, one group ahead.  The
+    // barrier at each group's end otherwise keeps all waves in step, all
+    // decoding (the matrix unit idle) and then all issuing MFMAs, with their
+    // memory requests in bursts.  (Measured at batch 256: 2-5% faster for
+    // r <= 4, with either pairing of waves into teams; at r = 5..8 the second
+    // copy of the loop spills registers, so those widths keep one team.)
+    const bool team_b = R <= 4 && ((w >> 2) & 1);
+    uint32_t W[32];      // the decoded weights of the group being computed
+    uint32_t s_nx = 0u;  // the scale of the next group (team B: loaded a group early)
+
     // Prologue: X and scales of the first group, its planes in flight.
     stage_x(g_begin, 0);
     uint32_t s_raw = srow[g_begin];
@@ -251,11 +263,16 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(R) : "memory");
     __builtin_amdgcn_s_barrier();
 
-    // One group: its weights decoded (the planes arrived during the previous
-    // group; the other workgroup on the compute unit keeps the matrix cores
-    // busy meanwhile), the next group's planes and X requested, then the
-    // chains over the batch tiles.
-    auto group = [&](int g, int qb) {
+    // One group: its weights decoded (team A; the planes arrived during the
+    // previous group), the next group's planes and X requested, then the
+    // chains over the batch tiles (team B then decodes the next group).  The
+    // team is a compile-time argument: each team runs its own copy of the
+    // loop, so the decoded weights are live across a group boundary in team
+    // B's copy only.
+    // (always inlined: six call sites, and a call would put the accumulators
+    // and the decoded weights in scratch memory)
+    auto group = [&](auto tb, int g, int qb) __attribute__((always_inline)) {
+        constexpr bool TB = decltype(tb)::value;
         const int gi = g - g_begin;
         if (gi > 0 && (gi & 7) == 0) consume(((gi >> 3) - 1) & 1);  // a block is complete
         if ((gi & 7) == 0) {
@@ -264,13 +281,14 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
                 (u32x4_t){0u, 0u, 0u, 0u};
         }
         const int gnext = min(g + 1, g_end - 1);
-        uint32_t W[32];
-        decode(W);
-        // (the planes of g are the oldest loads in flight; nothing may be
-        // requested ahead of the decode, or the wait for them waits for it too)
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t s_next = srow[gnext];
-        load_planes(gnext);
+        if constexpr (!TB) {
+            decode(W);
+            // (the planes of g are the oldest loads in flight; nothing may be
+            // requested ahead of the decode, or the wait for them waits for it too)
+            __builtin_amdgcn_sched_barrier(0);
+            s_nx = srow[gnext];
+            load_planes(gnext);
+        }
         const float s = nvalid ? __uint_as_float(s_raw << 16) : 0.f;
         reinterpret_cast<uint16_t *>(sbl + ((gi >> 3) & 1) * L::sblk)[tid * GW_CB + (gi & 7)] =
             (uint16_t)(nvalid ? s_raw : 0u);
@@ -367,21 +385,54 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
             dst[h * BM * GW_CB] = (uint16_t)(h ? mid : hi);
             dst[2 * BM * GW_CB] = (uint16_t)lo;
         }
-        s_raw = s_next;
         __builtin_amdgcn_sched_barrier(0);
-        // X of the next group and this group's corrections are in LDS for
-        // every wave after the barrier (the planes of g + 1, requested before
-        // the X blocks, have arrived too: loads complete in order).
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        if constexpr (TB) {
+            // the next group's weights (its planes came in during this group),
+            // then the planes and scale of the one after
+            decode(W);
+            __builtin_amdgcn_sched_barrier(0);
+            const int g2 = min(g + 2, g_end - 1);
+            const uint32_t s2 = srow[g2];
+            load_planes(g2);
+            s_raw = s_nx;
+            s_nx = s2;
+            __builtin_amdgcn_sched_barrier(0);
+            // X of the next group and this group's corrections are in LDS for
+            // every wave after the barrier; the R + 1 loads just issued (planes
+            // and scale of g + 2, after the X blocks) stay in flight: loads
+            // complete in order.
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(R + 1) : "memory");
+        } else {
+            s_raw = s_nx;
+            __builtin_amdgcn_sched_barrier(0);
+            // X of the next group and this group's corrections are in LDS for
+            // every wave after the barrier (the planes of g + 1, requested
+            // before the X blocks, have arrived too: loads complete in order).
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        }
         __builtin_amdgcn_s_barrier();
     };
 
-    int g = g_begin;
-    for (; g + 1 < g_end; g += 2) {
-        group(g, 0);
-        group(g + 1, 1);
-    }
-    if (g < g_end) group(g, 0);
+    auto run = [&](auto tb) __attribute__((always_inline)) {
+        if constexpr (decltype(tb)::value) {  // the first group's weights, the next group's planes
+            decode(W);
+            __builtin_amdgcn_sched_barrier(0);
+            const int g1 = min(g_begin + 1, g_end - 1);
+            s_nx = srow[g1];
+            load_planes(g1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        int g = g_begin;
+        for (; g + 1 < g_end; g += 2) {
+            group(tb, g, 0);
+            group(tb, g + 1, 1);
+        }
+        if (g < g_end) group(tb, g, 0);
+    };
+    if (team_b)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     // The last (possibly partial) block of corrections.
     consume(((g_end - 1 - g_begin) >> 3) & 1);
 
