@@ -40,7 +40,9 @@
 //    exact products, fp32 sums.
 //  - the waves rotate the order of their batch tiles so that the tiles whose
 //    corrections they form come first; one barrier per group hands over the X
-//    buffers and the corrections.
+//    buffers and the corrections.  For r <= 4 half the waves decode the next
+//    group right after their chains instead of at the group's start, so that
+//    the workgroup does not decode and multiply in lockstep.
 //  - where the output tiles leave CUs idle, k splits over workgroups into a
 //    caller workspace and a second launch adds the splits in order.
 #include <cstdio>

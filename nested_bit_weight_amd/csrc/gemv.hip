@@ -1,6 +1,7 @@
-// gemv.hip -- batch-1 dequant-GEMV (VALU), gfx950, single and grouped launches.
+// gemv.hip -- streaming dequant-GEMV for batch 1..4, gfx950, single and
+// grouped launches.
 //
-// y[i] = sum_j x[j] * s[i][j/128] * 2^(8-r) * (q_r[i][j] + 1/2 - 2^(r-1)),
+// y[b][i] = sum_j x[b][j] * s[i][j/128] * 2^(8-r) * (q_r[i][j] + 1/2 - 2^(r-1)),
 // the r-bit child of a sliceable parent (MatGPTQ: Efficient and Accurate
 // Inference over Nested Quantized Models, Abstract: lower precisions read
 // fewer bits of the weights; Figure 1: the kernels run at 2..8 bits).  The
@@ -11,7 +12,8 @@
 //
 // At batch 1 the product is bound by HBM (r/8 bytes of planes per weight, one
 // multiply-add per weight) and, at r <= 3, nearly as much by the VALU issue
-// rate of the decode.  The layout of the work:
+// rate of the decode; up to four batch rows share one decode (below).  The
+// layout of the work:
 //
 //  - a workgroup owns a range of T 16-row tiles of one product and all of k;
 //    its W waves split k into 4-group sets (wave w: sets w, w+W, ...).
@@ -19,16 +21,19 @@
 //    wave's four 16-lane quarters read 4 x 256 contiguous plane bytes per
 //    plane and tile with 128-bit loads.
 //  - each wave walks its (set, tile) steps as one stream with PD steps of
-//    planes and scales in flight; all loads are unconditional (clamped at the
-//    end), so the loads-in-flight count between a load and its use is static.
-//  - the activations are staged in LDS by each wave for its set; a set switch
-//    reloads the lane's MFMA operand from LDS without touching the memory
-//    pipeline.
+//    planes and scales in flight; the loads are unconditional (clamped at
+//    the end; on long tile runs a set's X comes with its first tile only),
+//    so the loads-in-flight count between a load and its use is static, and
+//    every address is a scalar base plus a fixed lane offset.
+//  - the activations are staged in LDS by each wave for its set, in a layout
+//    free of bank conflicts; a set switch reloads the lane's MFMA operand
+//    from LDS without touching the memory pipeline.
 //  - decode: bit-plane transpose network + one shift / and-or per bf16 pair
 //    (decode.h) on the VALU; the products on the matrix cores, with a block
-//    diagonal activation operand that keeps the set's four groups in four
-//    output rows (see gemv_tiles); the group scales are folded in fp32 once
-//    per (row, group), and the waves meet in LDS in a fixed order.
+//    diagonal activation operand that keeps the set's four groups -- of up
+//    to four batch rows -- in separate output rows (see gemv_tiles); the
+//    group scales are folded in fp32 once per (row, group), and the waves
+//    meet in LDS in a fixed order.
 #include <algorithm>
 #include <cstdio>
 
@@ -38,7 +43,7 @@
 namespace nbw {
 
 
-constexpr int GEMV_MAX_WAVES = 8;   // waves per workgroup (the launch picks 4 or 8)
+constexpr int GEMV_MAX_WAVES = 8;   // waves per workgroup
 constexpr int GEMV_ODD_WAVES = 4;   // waves per workgroup of the odd-group-count kernel
 constexpr int GEMV_MAX_TILES = 16;  // tiles per workgroup
 constexpr int GEMV_MAX_GROUP = 32;  // products per grouped launch
