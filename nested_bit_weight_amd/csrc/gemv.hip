@@ -188,21 +188,6 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
     const int my_sets = nsets > w ? (nsets - w + W - 1) / W : 0;
     const int U = my_sets * T;
 
-    // Zero this wave's partial sums (only this wave writes them until the
-    // final barrier) and its zero block.
-    zrun[lane] = 0u;
-    if (lane < 32) zrun[64 + lane] = 0u;
-    if (NBR > 1 || gg == 0)
-        for (int t = 0; t < T; ++t) red[(w * slots + t) * RW + (NBR > 1 ? lane : i)] = 0.f;
-
-    // Coefficient of this lane's pair sums in the group correction
-    // sum_k x_k * (1/2 - 2^(R-1) - offset_k): lane (i, gg) takes the pairs
-    // i, i+16, i+32, i+48 of its group, which share one offset.
-    float my_coef = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-        if (i == m) my_coef = pair_coef<R>(m);
-
     // Step loads: R plane chunks (row i, group 4*set + gg), the two aligned
     // 32-bit words of the scales of row i's four groups of the set, and the
     // lane's 16 bytes of the set's X of each batch row (the same chunks for
@@ -258,10 +243,26 @@ __device__ __forceinline__ void gemv_tiles(const uint16_t *__restrict__ x, int64
             ++ps;
         }
     };
-    if (U > 0) {
+    if (U > 0) {  // (first: everything below waits for nothing)
 #pragma unroll
         for (int j = 0; j < PD; ++j) load_step(j);
     }
+
+    // The zero run, and the partial sums of a wave without steps (any other
+    // wave stores every slot of its own with its first set; only this wave
+    // writes them until the final barrier).
+    zrun[lane] = 0u;
+    if (lane < 32) zrun[64 + lane] = 0u;
+    if (U == 0 && (NBR > 1 || gg == 0))
+        for (int t = 0; t < T; ++t) red[(w * slots + t) * RW + (NBR > 1 ? lane : i)] = 0.f;
+
+    // Coefficient of this lane's pair sums in the group correction
+    // sum_k x_k * (1/2 - 2^(R-1) - offset_k): lane (i, gg) takes the pairs
+    // i, i+16, i+32, i+48 of its group, which share one offset.
+    float my_coef = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        if (i == m) my_coef = pair_coef<R>(m);
 
     uint32_t X2[64];  // A operand: group gg of batch row i / 4's X if i % 4 == gg, else zeros
     // the set's group corrections and group sums of X (asymmetric term), for
