@@ -114,9 +114,10 @@ def test_rows_strided_and_bf16(nbw, out_dtype, batch):
 def test_long_tile_runs_load_x_once_per_set(nbw, batch):
     # 768 tiles over the CUs give each workgroup a run of 3 tiles, and 9 sets
     # over 8 waves two steps per tile: the variant that loads a set's X only
-    # with its first tile.  Sampled rows against the oracle, and the batch
-    # rows against their batch-1 launches bit for bit.
-    n, k = 12288, 4608
+    # with its first tile (the last tile ragged: 11 of 16 rows).  Sampled
+    # rows against the oracle, and the batch rows against their batch-1
+    # launches bit for bit.
+    n, k = 12283, 4608
     rng = np.random.default_rng(140 + batch)
     codes = synth.uniform_codes(n, k, rng)
     x_bits = synth.activations(batch, k, rng)
@@ -131,7 +132,7 @@ def test_long_tile_runs_load_x_once_per_set(nbw, batch):
         name = nbw.kernel_name(batch, n, k, r)
         print(f"long runs n={n} k={k} batch={batch} r={r}: {name}", flush=True)
         cus = torch.cuda.get_device_properties(0).multi_processor_count
-        if 2.5 * cus <= n // 16 < 3.5 * cus:  # (runs of 3 tiles on this device)
+        if 2.5 * cus <= (n + 15) // 16 < 3.5 * cus:  # (runs of 3 tiles on this device)
             assert name.endswith(", true>")
         y = nbw.qgemm(x, child, s, r)
         if batch > 1:
