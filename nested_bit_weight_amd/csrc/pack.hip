@@ -19,8 +19,18 @@
 
 namespace nbw {
 
-constexpr int PACK_GROUPS = 16;                        // groups per workgroup region
-constexpr int PACK_ROW_BYTES = PACK_GROUPS * 128 + 16; // LDS row pitch (+16: bank spread)
+constexpr int PACK_GROUPS = 16;                   // groups per workgroup region
+constexpr int PACK_ROW_BYTES = PACK_GROUPS * 128; // LDS row pitch
+// 16-byte chunk c of region row i sits at chunk c ^ pack_swz(i) of the row.
+// The LDS serves a 16-byte-per-lane access half a wave at a time over 128
+// four-byte banks (32 chunks); lanes of a half-wave that hit one bank at
+// different addresses conflict.  Phase 1 writes 32 consecutive chunks of one
+// row per half-wave: any XOR below 32 keeps them on 32 distinct banks.  Phase
+// 2 has the 16 rows of two neighbouring groups in a half-wave, reading chunks
+// 8 gl + e: the two groups differ in bit 3 of the chunk index, so the
+// swizzles of the 16 rows must differ in bits 0..2 and 4 and leave bit 3
+// clear -- (i & 7) | (i & 8) << 1 -- and all 32 reads land on distinct banks.
+__device__ __forceinline__ int pack_swz(int i) { return (i & 7) | ((i & 8) << 1); }
 
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ codes, int n, int k,
                                                    uint8_t *__restrict__ planes,
@@ -47,7 +57,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     };
     auto put16 = [&](int u, const u32x4_t &val) {
         const int i = u / vec_per_row, v = u % vec_per_row;
-        *reinterpret_cast<u32x4_t *>(lds + i * PACK_ROW_BYTES + 16 * v) = val;
+        *reinterpret_cast<u32x4_t *>(lds + i * PACK_ROW_BYTES + 16 * (v ^ pack_swz(i))) = val;
     };
     if (gcount == PACK_GROUPS) {
         constexpr int PER = 16 * PACK_GROUPS * 8 / 256;
@@ -64,13 +74,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     // Phase 2: thread -> (row i, group gl) chunk.
     const int i = tid & 15, gl = tid >> 4;
     if (gl >= gcount) return;
-    const uint8_t *src = lds + i * PACK_ROW_BYTES + gl * 128;
+    const uint8_t *src = lds + i * PACK_ROW_BYTES;
+    const int swz = pack_swz(i);
     uint32_t out[8][4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         uint32_t W[8];
-        const uint4 a = *reinterpret_cast<const uint4 *>(src + 32 * d);
-        const uint4 b = *reinterpret_cast<const uint4 *>(src + 32 * d + 16);
+        const uint4 a = *reinterpret_cast<const uint4 *>(src + 16 * ((8 * gl + 2 * d) ^ swz));
+        const uint4 b = *reinterpret_cast<const uint4 *>(src + 16 * ((8 * gl + 2 * d + 1) ^ swz));
         W[0] = a.x; W[1] = a.y; W[2] = a.z; W[3] = a.w;
         W[4] = b.x; W[5] = b.y; W[6] = b.z; W[7] = b.w;
         uint32_t P[8];
