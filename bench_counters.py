@@ -205,7 +205,7 @@ def _split_probe(kind, disp):
     return ref, per
 
 
-def pmc_summary(kind, folders, command_dirs=None):
+def pmc_summary(kind, folders):
     title, sources, prods = PROBES[kind]
     merged = {}      # product index -> {"main": {counter: [values]}, "extra": {counter: [values]}, ...}
     factors = {}
@@ -237,12 +237,13 @@ def pmc_summary(kind, folders, command_dirs=None):
         v = d.get(c)
         return sum(v) / len(v) if v else None
 
+    # (the recorded commands name the folders given, one per pass in order)
+    pass_dirs = list(folders) if len(folders) == len(PASSES) else [f"DIR_{p}" for p in PASSES]
     cmd_lines = []
-    for pname, ctrs in PASSES.items():
-        cmd_lines.append(f"  rocprofv3 --pmc {' '.join(ctrs)} -f csv -d gpurun_out/pmc_{kind}_{pname} "
+    for (pname, ctrs), d in zip(PASSES.items(), pass_dirs):
+        cmd_lines.append(f"  rocprofv3 --pmc {' '.join(ctrs)} -f csv -d {d} "
                          f"-- python3 bench.py --pmc-probe {kind}")
-    dirs = " ".join(f"gpurun_out/pmc_{kind}_{p}" for p in PASSES)
-    cmd_lines.append(f"  python3 bench.py --pmc-summary {kind} {dirs}")
+    cmd_lines.append(f"  python3 bench.py --pmc-summary {kind} {' '.join(folders)}")
     lines = [f"# Counters: {title}", "",
              "Commands (repository root, one MI355X; each --pmc pass in a run of its own, "
              "under `cd /tmp && export TMPDIR=/tmp` with absolute paths):", *cmd_lines, "",
