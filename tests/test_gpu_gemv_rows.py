@@ -44,7 +44,7 @@ def by_rows(nbw, x, child, s, r, **kw):
     return torch.cat([nbw.qgemm(x[b:b + 1], child, s, r, kernel="gemv", **kw) for b in range(x.shape[0])])
 
 
-@pytest.mark.parametrize("n,k", [(1000, 1024), (333, 4096), (16, 512)])
+@pytest.mark.parametrize("n,k", [(1000, 1024), (333, 4096), (16, 512), (7, 512)])
 @pytest.mark.parametrize("batch", [2, 3, 4, 5, 6, 9])
 def test_rows_match_batch1_launches_bitwise(nbw, n, k, batch):
     case = synth.random_case(n, k, batch, seed=100 + batch + k, recipe="gptq_like", outliers=True)
