@@ -31,8 +31,9 @@
 //    MFMA of the next chain), so every operand of the chain is exact in bf16.
 //  - the decode's constant offsets leave, per batch row and group, a
 //    correction sum_k x_k * (1/2 - 2^(r-1) - offset_k) (X only) times the
-//    group scale.  Each wave forms the corrections of NBT/4 batch tiles from the
-//    X fragments it reads anyway, splits each fp32 value exactly into three
+//    group scale.  Each of waves 0..3 forms the corrections of one batch tile
+//    from the X fragments it reads anyway (waves 4..7 read the same fragments
+//    and leave it to them), splits each fp32 value exactly into three
 //    bf16 parts, and parks them in LDS; every 8 groups the block of
 //    corrections enters the accumulators as a small bf16 product (corrections
 //    [batch row][part, group] times scales [part, group][weight row], the
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     constexpr int BM = L::BM;
     constexpr bool BYTES = R > 4;
     constexpr float POST = BYTES ? 1.0f : (float)(1 << (8 - R));
-    // batch tiles whose corrections this wave forms (waves w and w + NBT form
-    // the same ones and write the same values)
+    // batch tiles whose corrections a wave forms; waves w and w + NBT have the
+    // same ones, and only waves 0..3 form them
     constexpr int CT = 1;
 
     const int G = k >> 7;
@@ -254,7 +255,9 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     // memory requests in bursts.  (Measured at batch 256: 2-5% faster for
     // r <= 4, with either pairing of waves into teams; at r = 5..8 the second
     // copy of the loop spills registers, so those widths keep one team.)
-    const bool team_b = R <= 4 && ((w >> 2) & 1);
+    // Waves 4..7 (team B for r <= 4) leave the corrections to waves 0..3.
+    const bool upper = (w >> 2) & 1;
+    const bool team_b = R <= 4 && upper;
     uint32_t W[32];      // the decoded weights of the group being computed
     uint32_t s_nx = 0u;  // the scale of the next group (team B: loaded a group early)
 
@@ -273,8 +276,9 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     // B's copy only.
     // (always inlined: six call sites, and a call would put the accumulators
     // and the decoded weights in scratch memory)
-    auto group = [&](auto tb, int g, int qb) __attribute__((always_inline)) {
+    auto group = [&](auto tb, auto form, int g, int qb) __attribute__((always_inline)) {
         constexpr bool TB = decltype(tb)::value;
+        constexpr bool FORM = decltype(form)::value;  // this wave forms its tiles' corrections
         const int gi = g - g_begin;
         if (gi > 0 && (gi & 7) == 0) consume(((gi >> 3) - 1) & 1);  // a block is complete
         if ((gi & 7) == 0) {
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
                     const int nidx = idx + XD;
                     ring[idx % XD] = xfrag(qb, (nidx / 8 + CT * w) & (NBT - 1), nidx % 8);
                 }
-                if (pos < CT) {
+                if (FORM && pos < CT) {
                     cls[pos][gw_class<R>(j, 0)] = gw_dot2(one, a.x, cls[pos][gw_class<R>(j, 0)]);
                     cls[pos][gw_class<R>(j, 1)] = gw_dot2(one, a.y, cls[pos][gw_class<R>(j, 1)]);
                     cls[pos][gw_class<R>(j, 2)] = gw_dot2(one, a.z, cls[pos][gw_class<R>(j, 2)]);
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
         unsigned char *cbp = cb + ((gi >> 3) & 1) * L::cblk;
         const int slot = gi & 7;
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
+        for (int c = 0; c < (FORM ? CT : 0); ++c) {
             float corr = 0.f;
 #pragma unroll
             for (int a = 0; a < 7; ++a) {
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
         __builtin_amdgcn_s_barrier();
     };
 
-    auto run = [&](auto tb) __attribute__((always_inline)) {
+    auto run = [&](auto tb, auto form) __attribute__((always_inline)) {
         if constexpr (decltype(tb)::value) {  // the first group's weights, the next group's planes
             decode(W);
             __builtin_amdgcn_sched_barrier(0);
@@ -426,15 +430,17 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
         }
         int g = g_begin;
         for (; g + 1 < g_end; g += 2) {
-            group(tb, g, 0);
-            group(tb, g + 1, 1);
+            group(tb, form, g, 0);
+            group(tb, form, g + 1, 1);
         }
-        if (g < g_end) group(tb, g, 0);
+        if (g < g_end) group(tb, form, g, 0);
     };
     if (team_b)
-        run(std::true_type{});
+        run(std::true_type{}, std::false_type{});
+    else if (upper)
+        run(std::false_type{}, std::false_type{});
     else
-        run(std::false_type{});
+        run(std::false_type{}, std::true_type{});
     // The last (possibly partial) block of corrections.
     consume(((g_end - 1 - g_begin) >> 3) & 1);
 
