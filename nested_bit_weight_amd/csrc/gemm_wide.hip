@@ -148,6 +148,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     // batch tiles whose corrections a wave forms; waves w and w + NBT have the
     // same ones, and only waves 0..3 form them
     constexpr int CT = 1;
+    static_assert(2 * NBT == GW_WAVES, "waves w and w + NBT share their batch tiles");
 
     const int G = k >> 7;
     const int g_begin = blockIdx.z * gps;
@@ -253,8 +254,9 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     // barrier at each group's end otherwise keeps all waves in step, all
     // decoding (the matrix unit idle) and then all issuing MFMAs, with their
     // memory requests in bursts.  (Measured at batch 256: 2-5% faster for
-    // r <= 4, with either pairing of waves into teams; at r = 5..8 the second
-    // copy of the loop spills registers, so those widths keep one team.)
+    // r <= 4 on one box, with either pairing of waves into teams, the same
+    // speed on another; at r = 5..8 team B's copy of the loop spills
+    // registers, so those widths keep one team.)
     // Waves 4..7 (team B for r <= 4) leave the corrections to waves 0..3.
     const bool upper = (w >> 2) & 1;
     const bool team_b = R <= 4 && upper;
