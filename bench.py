@@ -604,6 +604,36 @@ def section_b4_16(torch, nbw, synth, args, layer, result, bytes_step):
     result["other_batches"] = other
 
 
+def mfma_rate_context(torch, nbw, reps=5):
+    """The matrix-unit rate loop (nbw_mfma_rate: v_mfma_f32_32x32x16_bf16 and nothing else, two waves per
+    SIMD on every compute unit) with random N(0, 1) bf16 operands and with all operands 1.0: the ceiling
+    the large-batch products meet on this chip and their kind of data (the clock under this load depends
+    on the data)."""
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    n = nbw.MFMA_RATE_OPS_BYTES // 2
+    operands = {"random": torch.randn(n, device="cuda", generator=gen).to(torch.bfloat16),
+                "constant": torch.ones(n, device="cuda", dtype=torch.bfloat16)}
+    sink = nbw.mfma_rate_sink()
+    iters = 1000
+    flops = nbw.mfma_rate_flops(sink, iters)
+    out = {}
+    for name, ops in operands.items():
+        nbw.mfma_rate(ops, 20, sink)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            nbw.mfma_rate(ops, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[f"{name}_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 1)
+    out["frac_of_peak_random"] = round(out["random_TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+    out["note"] = ("nbw_mfma_rate: 64 v_mfma_f32_32x32x16_bf16 per wave and round, four accumulator chains, "
+                   "operands cycling through 8 A and 8 B register fragments, no memory traffic")
+    return out
+
+
 def section_b256(torch, nbw, synth, args, layer, result):
     B = 256
     layer.add_batch(torch, synth, B)
@@ -619,21 +649,26 @@ def section_b256(torch, nbw, synth, args, layer, result):
     ach = t["flops"] / (t["us"] * 1e-6) / 1e12
     import bench_counters
     traffic = bench_counters.stored_traffic("gemm_b256", [(bench_counters.LLAMA, nm, B, r) for nm, r in t["products"]])
+    mrate = mfma_rate_context(torch, nbw)
     result["batch256"] = {
         "TFLOPs": round(tflops, 2), "frac_mfma": round(tflops / BF16_PEAK_TFLOPS, 4), "ms_per_step": round(ms, 5),
+        "frac_of_mfma_rate": round(tflops / mrate["random_TFLOPs"], 4),
         "steps": steps, "r": list(RS_B256),
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": round(traffic) if traffic else None,
                      "kernel": name, "avg_launch_us": round(t["us"] / t["launches"], 2),
                      "flops_per_launch": t["flops"] // t["launches"],
                      "products": [f"{nm} r={r}" for nm, r in t["products"]],
-                     "note": "a launch is the product's dispatch plus its second-pass add where k is split"},
+                     "note": "a launch is the product's dispatch plus its second-pass add where k is split",
+                     "frac_of_mfma_rate": round(ach / mrate["random_TFLOPs"], 4)},
         "gpu_clock": clock,
+        "mfma_rate": mrate,
         "per_shape": [{"linear": nm, "r": r, "us": round(d["us"], 2),
                        "TFLOPs": round(2 * B * d["n"] * d["k"] / (d["us"] * 1e-6) / 1e12, 1),
                        "kernel": d["kernel"]}
                       for (nm, r), d in sorted(d256.items())]}
-    log(f"batch 256: {tflops:.1f} TFLOP/s over {steps} steps; {name} {ach:.1f} TFLOP/s; clock {clock.get('sclk_mhz')}")
+    log(f"batch 256: {tflops:.1f} TFLOP/s over {steps} steps; {name} {ach:.1f} TFLOP/s; clock {clock.get('sclk_mhz')}; "
+        f"matrix-unit rate loop {mrate['random_TFLOPs']} TFLOP/s (random operands), {mrate['constant_TFLOPs']} (constant)")
     layer.drop_batch(B)
 
 

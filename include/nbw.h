@@ -285,6 +285,30 @@ nbw_status nbw_unpack_codes(const nbw_wview *w, int32_t r, uint8_t *codes_out, v
 int32_t nbw_stream_sink_words(void);
 nbw_status nbw_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
+/* Matrix-unit reference for the products beyond batch one (MatGPTQ:
+ * Efficient and Accurate Inference over Nested Quantized Models, Abstract:
+ * kernels that serve batch sizes beyond one; at batch 128-256 the products
+ * are bound by v_mfma_f32_32x32x16_bf16): one launch of `iters` rounds in
+ * which every wave issues 64 of those instructions and nothing else (four
+ * independent accumulator chains, two waves per SIMD, one workgroup of 8
+ * waves per compute unit), the operands cycling through 8 A and 8 B
+ * fragments held in registers.  Its rate is the ceiling the products are
+ * measured against on the same chip and operand data.
+ * ops: device pointer, 16-byte aligned, 16 KB: fragment f (0..15) of lane l
+ * (0..63) is the 16 bytes at (f * 64 + l) * 16, eight bf16 values in the
+ * instruction's operand layout; f < 8 are A operands, f >= 8 B operands.
+ * Round MFMA s (0..63) multiplies A fragment s % 8 by B fragment (s / 8) % 8
+ * into accumulator s % 4.  iters >= 1.
+ * sink: device float array of nbw_mfma_rate_sink_floats() floats
+ * (caller-owned), fully written: float t is thread t's sum of its four
+ * accumulators (every wave computes the same values).  A launch performs
+ * (nbw_mfma_rate_sink_floats() / 64) * iters * 64 * 32768 flops.
+ * Errors: NBW_EINVAL (null pointer, iters < 1), NBW_EALIGN, NBW_EHIP (no
+ * device or launch failed; nbw_mfma_rate_sink_floats then returns -1).
+ * Asynchronous on `stream`. */
+int64_t nbw_mfma_rate_sink_floats(void);
+nbw_status nbw_mfma_rate(const void *ops, int32_t iters, float *sink, void *stream);
+
 /* On-disk form of a sliceable parent (host only, no device work).  The r-bit
  * child loads exactly r bits per weight (MatGPTQ: Efficient and Accurate
  * Inference over Nested Quantized Models, Abstract; Table 1, row "Exact r-bit

@@ -74,6 +74,7 @@ EXPORTS = ("nbw_plane_bytes", "nbw_packed_bytes", "nbw_pack_bitplanes", "nbw_mak
            "nbw_slice_view", "nbw_qgemm", "nbw_qgemm_kernel", "nbw_qgemm_ex", "nbw_qgemm_noalloc",
            "nbw_qgemm_workspace_bytes", "nbw_qgemm_grouped",
            "nbw_choose_codes", "nbw_unpack_codes", "nbw_stream_sink_words", "nbw_stream_read",
+           "nbw_mfma_rate_sink_floats", "nbw_mfma_rate",
            "nbw_file_prefix_bytes", "nbw_file_header", "nbw_file_parse",
            "nbw_kernel_name", "nbw_status_str", "nbw_last_hip_error", "nbw_version")
 
@@ -117,6 +118,10 @@ def _lib():
         lib.nbw_stream_sink_words.restype = i32
         lib.nbw_stream_read.argtypes = [vp, i64, vp, vp]
         lib.nbw_stream_read.restype = ctypes.c_int
+        lib.nbw_mfma_rate_sink_floats.argtypes = []
+        lib.nbw_mfma_rate_sink_floats.restype = i64
+        lib.nbw_mfma_rate.argtypes = [vp, i32, vp, vp]
+        lib.nbw_mfma_rate.restype = ctypes.c_int
         lib.nbw_status_str.argtypes = [ctypes.c_int]
         lib.nbw_status_str.restype = ctypes.c_char_p
         lib.nbw_last_hip_error.argtypes = []
@@ -472,6 +477,32 @@ def stream_read(src: torch.Tensor, nbytes: int, sink: torch.Tensor) -> None:
                                   ctypes.c_void_p(sink.data_ptr()), _stream(src)), "nbw_stream_read")
 
 
+MFMA_RATE_OPS_BYTES = 16 * 64 * 16  # 16 fragments x 64 lanes x 16 bytes
+
+
+def mfma_rate_sink(device=None) -> torch.Tensor:
+    """A sink buffer for mfma_rate (nbw_mfma_rate_sink_floats() floats)."""
+    nf = _lib().nbw_mfma_rate_sink_floats()
+    if nf < 0:
+        raise NBWError("nbw_mfma_rate_sink_floats: no device")
+    return torch.empty(nf, dtype=torch.float32, device=device if device is not None else "cuda")
+
+
+def mfma_rate_flops(sink: torch.Tensor, iters: int) -> int:
+    """Flops of one mfma_rate launch of `iters` rounds (64 MFMAs of 32768 flops per wave and round)."""
+    return sink.numel() // 64 * iters * 64 * 32768
+
+
+def mfma_rate(ops: torch.Tensor, iters: int, sink: torch.Tensor) -> None:
+    """Launch the matrix-unit rate loop on the 16 KB of operand fragments in ops (compute reference)."""
+    if ops.numel() * ops.element_size() < MFMA_RATE_OPS_BYTES:
+        raise ValueError(f"mfma_rate: ops needs {MFMA_RATE_OPS_BYTES} bytes")
+    if sink.dtype != torch.float32 or sink.numel() < _lib().nbw_mfma_rate_sink_floats():
+        raise ValueError(f"mfma_rate: sink needs {_lib().nbw_mfma_rate_sink_floats()} float32 values")
+    _check(_lib().nbw_mfma_rate(ctypes.c_void_p(ops.data_ptr()), int(iters), ctypes.c_void_p(sink.data_ptr()),
+                                _stream(ops)), "nbw_mfma_rate")
+
+
 def file_prefix_bytes(n: int, k: int, r: int) -> int:
     """Bytes at the head of a parent file that hold everything an r-bit child needs."""
     v = _lib().nbw_file_prefix_bytes(n, k, r)
@@ -549,6 +580,6 @@ def version() -> str:
 
 
 __all__ = ["pack_bitplanes", "slice_view", "save_parent", "load_child", "file_info",
-           "file_prefix_bytes", "qgemm", "QgemmCall", "qgemm_grouped", "workspace_bytes", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "plane_bytes",
+           "file_prefix_bytes", "qgemm", "QgemmCall", "qgemm_grouped", "workspace_bytes", "choose_codes", "unpack_codes", "stream_read", "stream_sink", "mfma_rate", "mfma_rate_sink", "mfma_rate_flops", "plane_bytes",
            "packed_bytes", "PackedWeight", "NBWError", "KERNELS", "library", "kernel_name",
            "version"]

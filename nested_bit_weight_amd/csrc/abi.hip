@@ -375,6 +375,22 @@ nbw_status nbw_stream_read(const void *src, int64_t bytes, uint32_t *sink, void 
     return e == hipSuccess ? NBW_OK : hip_failed(e);
 }
 
+int64_t nbw_mfma_rate_sink_floats(void) {
+    int cus = 0;
+    if (cu_count(&cus) != NBW_OK) return -1;
+    return nbw::mfma_rate_threads(cus);
+}
+
+nbw_status nbw_mfma_rate(const void *ops, int32_t iters, float *sink, void *stream) {
+    if (!ops || !sink || iters < 1) return NBW_EINVAL;
+    if (!aligned(ops, 16) || !aligned(sink, 4)) return NBW_EALIGN;
+    int cus = 0;
+    const nbw_status st = cu_count(&cus);
+    if (st != NBW_OK) return st;
+    hipError_t e = nbw::launch_mfma_rate(ops, iters, sink, cus, (hipStream_t)stream);
+    return e == hipSuccess ? NBW_OK : hip_failed(e);
+}
+
 const char *nbw_kernel_name(int64_t batch, int64_t n, int64_t k, int32_t r, nbw_kernel kernel) {
     thread_local char buf[96];
     if (!shape_ok(n, k) || batch < 1 || r < 1 || r > 8 || kernel < NBW_KERNEL_AUTO ||

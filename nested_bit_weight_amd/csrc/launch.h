@@ -66,6 +66,8 @@ int64_t gemm_workspace_bytes(const QgemmArgs &a, int cu_count);
 // XOR word per wave into sink (stream_sink_words() words).
 int stream_sink_words();
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+int mfma_rate_threads(int cu_count);
+hipError_t launch_mfma_rate(const void *ops, int iters, float *sink, int cu_count, hipStream_t stream);
 
 // Grouped batch-1 launch: several products (each with its own r) as one
 // dispatch.  Eligible problems: batch 1, shapes the streaming kernel takes.

@@ -201,6 +201,16 @@ def test_stream_read_validation(lib):
     assert lib.nbw_stream_read(vp(FAKE), 1024, vp(FAKE + 2), None) == EALIGN
 
 
+def test_mfma_rate_validation(lib):
+    # argument checks come before the device is queried (no GPU here)
+    vp = ctypes.c_void_p
+    assert lib.nbw_mfma_rate(None, 1, vp(FAKE), None) == EINVAL
+    assert lib.nbw_mfma_rate(vp(FAKE), 1, None, None) == EINVAL
+    assert lib.nbw_mfma_rate(vp(FAKE), 0, vp(FAKE), None) == EINVAL
+    assert lib.nbw_mfma_rate(vp(FAKE + 8), 1, vp(FAKE), None) == EALIGN
+    assert lib.nbw_mfma_rate(vp(FAKE), 1, vp(FAKE + 2), None) == EALIGN
+
+
 def test_noalloc_rejects_before_any_device_work(lib):
     p = ctypes.c_void_p
     _, v = _view(lib)
