@@ -254,7 +254,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) void gemm_wide_kernel(
     // barrier at each group's end otherwise keeps all waves in step, all
     // decoding (the matrix unit idle) and then all issuing MFMAs, with their
     // memory requests in bursts.  (Measured at batch 256: 2-5% faster for
-    // r <= 4 on one box, with either pairing of waves into teams, the same
+    // r <= 4 on one MI355X, with either pairing of waves into teams, the same
     // speed on another; at r = 5..8 team B's copy of the loop spills
     // registers, so those widths keep one team.)
     // Waves 4..7 (team B for r <= 4) leave the corrections to waves 0..3.
