@@ -406,7 +406,8 @@ def trace_summary(section, folder, command):
     lines = [f"# Kernel trace: bench.py --only {section}", "",
              "Commands (repository root, one MI355X):", "", "```", command,
              f"python3 bench.py --trace-summary {section} {folder}", "```", "",
-             "Every qgemm dispatch of the run (warm-up, graph capture and replay, per-product timing).  A second-pass add "
+             "Every dispatch of the run: the qgemm kernels (warm-up, graph capture and replay, per-product timing) and "
+             "the reference launches timed beside them (nbw::stream_read_kernel, nbw::mfma_rate_kernel).  A second-pass add "
              "of a split launch is attributed to the launch before it: avg us is the main dispatch, add us its add "
              "spread over all calls of the group, launch us the two together (what the bench's HIP events time per "
              "product).", "",
