@@ -358,7 +358,10 @@ def b1_products_table(durs):
     for (nm, r), d in sorted(durs.items()):
         pb = r * d["n"] * d["k"] // 8
         gbs = pb / (d["us"] * 1e-6) / 1e9
+        # planes, plus the scales (2 bytes per 128 weights), X (bf16) and Y (fp32) of one batch row
+        eff = pb + d["n"] * d["k"] // 64 + 2 * d["k"] + 4 * d["n"]
         e = {"linear": nm, "r": r, "us": round(d["us"], 2), "GBps": round(gbs, 1),
+             "GBps_effective": round(eff / (d["us"] * 1e-6) / 1e9, 1),
              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "ge_5us_at_peak": pb / (HBM_PEAK_GBS * 1e3) >= 5.0,
              "kernel": d["kernel"], "rotation_copies": d["copies"]}
         if "floor_us" in d:
@@ -393,7 +396,7 @@ def host_info():
 
 
 def clock_under_load(torch, replay, ms_per_replay, seconds=1.5):
-    """The shader clock rocm-smi reports while ~seconds of replays run."""
+    """The shader clock, the package power and the power cap rocm-smi reports while ~seconds of replays run."""
     n = max(1, int(seconds * 1e3 / max(ms_per_replay, 1e-3)))
     torch.cuda.synchronize()
     for i in range(n):
@@ -401,17 +404,28 @@ def clock_under_load(torch, replay, ms_per_replay, seconds=1.5):
     time.sleep(min(0.5, seconds / 3))
     out = ""
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower"], capture_output=True,
+                             text=True, timeout=30).stdout
     except (OSError, subprocess.SubprocessError):
         pass
     torch.cuda.synchronize()
+    res = {"sclk_mhz": None, "source": "rocm-smi --showclocks --showpower --showmaxpower during batch-256 replays"}
     for line in out.splitlines():
-        if "sclk" in line.lower():
+        low = line.lower()
+        if "sclk" in low and res["sclk_mhz"] is None:
             m = re.search(r"(\d+)\s*mhz", line, re.I)
             if m:
-                return {"sclk_mhz": int(m.group(1)), "source": "rocm-smi --showclocks during batch-256 replays",
-                        "line": line.strip()}
-    return {"sclk_mhz": None, "source": "rocm-smi --showclocks gave no sclk line"}
+                res["sclk_mhz"] = int(m.group(1))
+                res["line"] = line.strip()
+        elif "max graphics package power" in low:
+            m = re.search(r":\s*([\d.]+)\s*$", line.strip())
+            if m:
+                res["power_cap_w"] = float(m.group(1))
+        elif "graphics package power" in low:
+            m = re.search(r":\s*([\d.]+)\s*$", line.strip())
+            if m:
+                res["power_w"] = float(m.group(1))
+    return res
 
 
 # ---------------------------------------------------------------- sections
