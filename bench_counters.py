@@ -21,6 +21,7 @@ import csv
 import glob
 import hashlib
 import os
+import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -390,19 +391,21 @@ def trace_summary(section, folder, command):
                 g["adds"] += 1
             continue
         key = (name, "x".join(r[c] for c in gcols))
-        gn = by_name.setdefault(name, {"ns": 0, "calls": 0, "add_ns": 0, "adds": 0})
-        gg = by_grid.setdefault(key, {"ns": 0, "calls": 0, "add_ns": 0, "adds": 0})
+        gn = by_name.setdefault(name, {"ns": 0, "calls": 0, "add_ns": 0, "adds": 0, "all": []})
+        gg = by_grid.setdefault(key, {"ns": 0, "calls": 0, "add_ns": 0, "adds": 0, "all": []})
         if key not in order:
             order.append(key)
         for g in (gn, gg):
             g["ns"] += ns
             g["calls"] += 1
+            g["all"].append(ns)
         last = (gn, gg)
 
     def row(label, g):
         avg = g["ns"] / g["calls"] / 1e3
+        med = statistics.median(g["all"]) / 1e3
         add = g["add_ns"] / g["calls"] / 1e3
-        return f"| {label} | {g['calls']} | {avg:.2f} | {g['adds']} | {add:.2f} | {avg + add:.2f} |"
+        return f"| {label} | {g['calls']} | {avg:.2f} | {med:.2f} | {g['adds']} | {add:.2f} | {avg + add:.2f} |"
     lines = [f"# Kernel trace: bench.py --only {section}", "",
              "Commands (repository root, one MI355X):", "", "```", command,
              f"python3 bench.py --trace-summary {section} {folder}", "```", "",
@@ -410,15 +413,15 @@ def trace_summary(section, folder, command):
              "the reference launches timed beside them (nbw::stream_read_kernel, nbw::mfma_rate_kernel).  A second-pass add "
              "of a split launch is attributed to the launch before it: avg us is the main dispatch, add us its add "
              "spread over all calls of the group, launch us the two together (what the bench's HIP events time per "
-             "product).", "",
-             "| kernel | calls | avg us | adds | add us | launch us |", "|---|---|---|---|---|---|"]
+             "product); median us is the median main dispatch.", "",
+             "| kernel | calls | avg us | median us | adds | add us | launch us |", "|---|---|---|---|---|---|---|"]
     out = {}
     for name, g in sorted(by_name.items(), key=lambda kv: -kv[1]["ns"]):
         lines.append(row(f"`{name}`", g))
         out[name] = {"calls": g["calls"], "avg_us": g["ns"] / g["calls"] / 1e3,
                      "launch_us": (g["ns"] + g["add_ns"]) / g["calls"] / 1e3}
     lines += ["", "By kernel and grid (work-items x, y, z):", "",
-              "| kernel, grid | calls | avg us | adds | add us | launch us |", "|---|---|---|---|---|---|"]
+              "| kernel, grid | calls | avg us | median us | adds | add us | launch us |", "|---|---|---|---|---|---|---|"]
     for key in order:
         lines.append(row(f"`{key[0]}` {key[1]}", by_grid[key]))
     path = os.path.join(PROFILES, f"trace_{section}.md")
