@@ -152,4 +152,6 @@ def test_trace_summary_attributes_the_split_add(tmp_path, monkeypatch):
     assert abs(g["avg_us"] - 60.0) < 1e-9
     assert abs(g["launch_us"] - 62.0) < 1e-9     # (4 x 100 + 4 x (20 + 4)) / 8
     text = open(tmp_path / "trace_b256.md").read()
-    assert "| `nbw::gemm_wide_kernel<8, 4>` 8192x2x1 | 4 | 20.00 | 4 | 4.00 | 24.00 |" in text
+    # avg, median, adds, add spread over the calls, launch
+    assert "| `nbw::gemm_wide_kernel<8, 4>` | 8 | 60.00 | 60.00 | 4 | 2.00 | 62.00 |" in text
+    assert "| `nbw::gemm_wide_kernel<8, 4>` 8192x2x1 | 4 | 20.00 | 20.00 | 4 | 4.00 | 24.00 |" in text
