@@ -47,6 +47,21 @@ def test_rotation_rule():
         assert (c - 1) * nb >= bench.ROTATE_BYTES > (c - 2) * nb
 
 
+def test_b1_products_table_bytes():
+    import bench
+    # Llama-3.1-8B down at r = 3 in 10 us: planes 3nk/8; effective adds the scales
+    # (2 bytes per 128 weights), one bf16 row of X and one fp32 row of Y
+    n, k = 4096, 14336
+    durs = {("down", 3): {"n": n, "k": k, "us": 10.0, "kernel": "kern", "copies": 5, "floor_us": 8.0}}
+    (e,) = bench.b1_products_table(durs)
+    planes = 3 * n * k // 8
+    assert e["GBps"] == round(planes / 10e-6 / 1e9, 1)
+    assert e["GBps_effective"] == round((planes + n * k // 64 + 2 * k + 4 * n) / 10e-6 / 1e9, 1)
+    assert e["frac_hbm"] == round(planes / 10e-6 / 1e9 / bench.HBM_PEAK_GBS, 4)
+    assert e["frac_of_read_floor"] == 0.8 and e["read_floor_us"] == 8.0
+    assert e["ge_5us_at_peak"] == (planes / (bench.HBM_PEAK_GBS * 1e3) >= 5.0)
+
+
 def _write_counters(path, rows):
     """rows: (dispatch id, kernel, counter, value, start ns, end ns)"""
     os.makedirs(os.path.join(path, "host"), exist_ok=True)
